@@ -1,0 +1,156 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) hot path for MI355X (gfx950).
+ *
+ * The path, as the pages state the problem (MarkTechPost, "DeepSeek V3.2-Exp Cuts
+ * Long-Context Costs with DeepSeek Sparse Attention (DSA) While Maintaining
+ * Benchmark Parity": two-tier pipeline "FP8 index -> top-k selection -> sparse core
+ * attention"; maplevalley.com.cn news 1594152, section "1. 细粒度稀疏架构": a
+ * lightning indexer scores every preceding token and each query keeps only k
+ * key/value pairs, O(L^2) -> O(Lk)):
+ *
+ *   1. dsa_index_scores       I[r, s] for every query row r and candidate s < n_r
+ *   2. dsa_topk               the k best s per row (ties -> lower s), -1 padded
+ *   3. dsa_sparse_mla_decode  MLA in MQA mode over the kept latent rows, one query
+ *      dsa_sparse_mla_prefill token per sequence (decode) or every token (prefill)
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned,
+ *     densely packed in the documented layout (row-major, last index fastest).
+ *   - The library never allocates, frees or synchronises.  Every call only enqueues
+ *     kernels on `stream` and returns; results are valid once the stream reaches them.
+ *   - Arguments are validated on the host before anything is launched; a validation
+ *     error returns its status and enqueues nothing.  Device-side values (indices,
+ *     lengths, page-table entries) are not validated: out-of-range values are
+ *     undefined behaviour.  A failed launch returns DSA_ERR_LAUNCH.
+ *   - Calls are stateless and thread-safe.  Two calls that share a workspace must
+ *     not overlap in time (same stream, or synchronised).
+ *   - Dtypes: DSA_E4M3 is OCP FP8 E4M3 ("e4m3fn": bias 7, max 448, no inf);
+ *     DSA_BF16 is bfloat16; DSA_F32 is IEEE binary32.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,        /* a required pointer is NULL                              */
+  DSA_ERR_SHAPE = 2,       /* a size is <= 0, inconsistent, or exceeds a stated limit  */
+  DSA_ERR_DTYPE = 3,       /* dtype not accepted by this entry point                   */
+  DSA_ERR_WORKSPACE = 4,   /* workspace pointer NULL or smaller than required          */
+  DSA_ERR_LAUNCH = 5,      /* the HIP runtime reported an error after launching        */
+  DSA_ERR_UNSUPPORTED = 6  /* valid but unsupported combination (e.g. page size % 16)  */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_E4M3 = 2 } dsa_dtype;
+
+/*
+ * A per-token cache of one tensor (indexer keys, or MLA latent rows), either
+ *   contiguous: row (b, s) at  data + (b * seq_stride + s) * D          (block_table == NULL)
+ *   paged:      row (b, s) at  data + (block_table[b * max_pages + s / page_size] * page_size
+ *                                      + s % page_size) * D
+ * D is the row width given to the call.  `scale` (indexer keys only) is the per-token
+ * fp32 dequantisation scale with the same addressing and a width of one float; NULL
+ * means 1.  Pages hold 64 tokens in the paged workloads (the pages do not fix a size).
+ */
+typedef struct {
+  const void* data;
+  const float* scale;
+  const int32_t* block_table;
+  int32_t page_size;
+  int32_t max_pages;
+  int64_t seq_stride;
+} dsa_cache;
+
+/*
+ * dsa_index_scores -- lightning-indexer scores (first tier of the DSA pipeline:
+ * "FP8 index", MarkTechPost article above; "Lightning Indexer", maplevalley article
+ * section 1).  The pages do not print the formula; this library computes
+ *
+ *   scores[r * ld + s] = k_scale[seq, s] * q_scale[r] * sum_{j < H_I} w[r, j] * max(0, q[r, j, :] . k[seq, s, :])
+ *
+ * for seq = row_seq[r] and every s in [0, n_r), n_r = row_pos[r] + 1 (the query's own
+ * token is a candidate).  Entries s >= n_r of a score row are left untouched.
+ *
+ *   dt        DSA_E4M3: q and keys are e4m3 codes (fast path: H_I == 64, d_I == 128,
+ *             paged page_size % 16 == 0); DSA_F32: q and keys are fp32 (any shape).
+ *   q         [R, H_I, d_I]          q_scale [R] or NULL (= 1)     w [R, H_I] fp32
+ *   keys      cache of rows of width d_I (+ per-token scale)
+ *   row_seq   [R] int32 sequence of each row      row_pos [R] int32 position of each row
+ *   scores    [R, ld] fp32 output; ld >= the cache's longest sequence
+ *             (seq_stride, or max_pages * page_size when paged)
+ * Decode: row r = sequence r, row_pos = L_r - 1.  Prefill of one sequence: row_seq = 0,
+ * row_pos = t.
+ */
+dsa_status dsa_index_scores(dsa_dtype dt, const void* q, const float* q_scale, const float* w,
+                            const dsa_cache* keys, const int32_t* row_seq, const int32_t* row_pos,
+                            int R, int H_I, int d_I, float* scores, int64_t ld, hipStream_t stream);
+
+/*
+ * dsa_topk -- per-row top-k token selection (maplevalley article section 1: "Top-k
+ * Token Selection", each query keeps k key/value pairs; tellworld "What happened":
+ * token-level selection; MarkTechPost "Training signal": k = 2048).
+ *
+ * For row r with n = n_valid[r] candidates (scores[r * ld + s], s < n): if n <= k all
+ * n indices are kept; otherwise the k largest, ties broken towards the lower index
+ * (-0.0 ties with +0.0; NaN scores are undefined behaviour).  idx[r * k + j] holds the
+ * kept indices in ascending order in slots j < min(k, n) and -1 in the rest.
+ *
+ *   scores [R, ld] fp32      n_valid [R] int32, 0 <= n_valid[r] <= ld
+ *   idx    [R, k] int32 output
+ *   ws     device workspace of at least dsa_topk_workspace_size(R, ld, k) bytes
+ * Limits: k <= 16384, ld <= 2^24.
+ */
+size_t dsa_topk_workspace_size(int R, int64_t ld, int k);
+dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
+                    int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dsa_sparse_mla_decode -- sparse core attention for one new token per sequence:
+ * MLA in MQA mode (MarkTechPost "Instantiation": each latent KV entry is shared across
+ * all query heads).  For sequence b and head h, over S_b = { idx[b, j] : idx[b, j] >= 0 }:
+ *
+ *   z_s = softmax_scale * q[b, h, :] . kv[b, s, :]          (all Dqk columns)
+ *   out[b, h, :] = sum_s softmax(z)_s * kv[b, s, :Dv]        (value = first Dv columns)
+ *   lse[b, h]    = log sum_s exp(z_s)                         (natural log)
+ * An empty S_b gives out = 0 and lse = -inf.
+ *
+ *   dt     DSA_BF16: q, kv, out bf16 (fast path: H % 64 == 0, Dqk == 576, Dv == 512,
+ *          paged page_size any); DSA_F32: fp32 (any shape with Dv <= Dqk <= 1024)
+ *   q      [B, H, Dqk]     kv cache of rows of width Dqk      idx [B, k] int32
+ *   out    [B, H, Dv]      lse [B, H] fp32 or NULL
+ *   ws     device workspace of at least dsa_sparse_mla_decode_workspace_size(...) bytes
+ *          (split-KV partials); may be NULL when that size is 0
+ */
+size_t dsa_sparse_mla_decode_workspace_size(int B, int H, int Dv, int k);
+dsa_status dsa_sparse_mla_decode(dsa_dtype dt, const void* q, const dsa_cache* kv,
+                                 const int32_t* idx, int B, int H, int Dqk, int Dv, int k,
+                                 float softmax_scale, void* out, float* lse, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dsa_sparse_mla_prefill -- the same attention for every token t of one sequence,
+ * each over its own kept set S_t = { idx[t, j] >= 0 } (causal selection is the
+ * caller's: dsa_topk with n_valid[t] = t + 1 keeps only s <= t).
+ *
+ *   q [T, H, Dqk]   kv [T, Dqk] (contiguous latent rows of the sequence)   idx [T, k]
+ *   out [T, H, Dv]  lse [T, H] fp32 or NULL
+ * dt and shape rules as for dsa_sparse_mla_decode.
+ */
+dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,
+                                  int T, int H, int Dqk, int Dv, int k, float softmax_scale,
+                                  void* out, float* lse, hipStream_t stream);
+
+/* Static text for a status code ("DSA_OK", ...); never NULL. */
+const char* dsa_status_string(dsa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

@@ -1,0 +1,167 @@
+"""Python binding of libdsa.so, the MI355X (gfx950) DeepSeek Sparse Attention hot path.
+
+The functions mirror the C ABI of include/dsa.h one to one and do argument
+marshalling only: every step of the path runs in the library's HIP kernels.
+PyTorch supplies device memory and the current HIP stream.  Importing works without
+the built library (so host-only code can inspect it); any call then raises
+`DSALibraryMissing` -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "DSAError", "DSALibraryMissing", "Cache", "F32", "BF16", "E4M3", "LIB_PATH", "lib",
+    "dsa_index_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_decode",
+    "dsa_sparse_mla_decode_workspace_size", "dsa_sparse_mla_prefill", "dsa_status_string",
+    "exported_symbols",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+F32, BF16, E4M3 = 0, 1, 2
+_STATUS = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_DTYPE", "DSA_ERR_WORKSPACE",
+           "DSA_ERR_LAUNCH", "DSA_ERR_UNSUPPORTED"]
+
+
+class DSAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        name = _STATUS[status] if 0 <= status < len(_STATUS) else f"status {status}"
+        super().__init__(f"{fn} failed: {name}")
+
+
+class DSALibraryMissing(RuntimeError):
+    pass
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("seq_stride", ctypes.c_int64)]
+
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "dsa_index_scores": (_i32, [_i32, _vp, _vp, _vp, ctypes.POINTER(_Cache), _vp, _vp, _i32, _i32,
+                                _i32, _vp, _i64, _vp]),
+    "dsa_topk_workspace_size": (_sz, [_i32, _i64, _i32]),
+    "dsa_topk": (_i32, [_vp, _i64, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "dsa_sparse_mla_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "dsa_sparse_mla_decode": (_i32, [_i32, _vp, ctypes.POINTER(_Cache), _vp, _i32, _i32, _i32, _i32,
+                                     _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "dsa_sparse_mla_prefill": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                      _vp, _vp]),
+    "dsa_status_string": (ctypes.c_char_p, [_i32]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdsa.so (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise DSALibraryMissing(
+                f"{LIB_PATH} is not built; run long_context_sparse_06_amd.build.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+# --------------------------------------------------------------------------- helpers
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("DSA tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("DSA tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise DSAError(fn, st)
+
+
+class Cache:
+    """A contiguous or paged per-token cache (see dsa_cache in include/dsa.h)."""
+
+    def __init__(self, data, scale=None, block_table=None, page_size: int = 0,
+                 seq_stride: int = 0):
+        self.data, self.scale, self.block_table = data, scale, block_table
+        self.page_size = int(page_size)
+        self.max_pages = int(block_table.shape[1]) if block_table is not None else 0
+        self.seq_stride = int(seq_stride)
+
+    def _c(self) -> _Cache:
+        return _Cache(_ptr(self.data), _ptr(self.scale), _ptr(self.block_table), self.page_size,
+                      self.max_pages, self.seq_stride)
+
+
+# --------------------------------------------------------------------------- the ABI
+def dsa_status_string(status: int) -> str:
+    return lib().dsa_status_string(status).decode()
+
+
+def dsa_index_scores(dt: int, q, q_scale, w, keys: Cache, row_seq, row_pos, R: int, H_I: int,
+                     d_I: int, scores, ld: int, stream=None):
+    c = keys._c()
+    _check("dsa_index_scores", lib().dsa_index_scores(
+        dt, _ptr(q), _ptr(q_scale), _ptr(w), ctypes.byref(c), _ptr(row_seq), _ptr(row_pos), R, H_I,
+        d_I, _ptr(scores), ld, _stream(stream)))
+
+
+def dsa_topk_workspace_size(R: int, ld: int, k: int) -> int:
+    return int(lib().dsa_topk_workspace_size(R, ld, k))
+
+
+def dsa_topk(scores, ld: int, n_valid, R: int, k: int, idx, ws=None, ws_bytes: int = 0, stream=None):
+    if ws is not None and not ws_bytes:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check("dsa_topk", lib().dsa_topk(_ptr(scores), ld, _ptr(n_valid), R, k, _ptr(idx), _ptr(ws),
+                                      ws_bytes, _stream(stream)))
+
+
+def dsa_sparse_mla_decode_workspace_size(B: int, H: int, Dv: int, k: int) -> int:
+    return int(lib().dsa_sparse_mla_decode_workspace_size(B, H, Dv, k))
+
+
+def dsa_sparse_mla_decode(dt: int, q, kv: Cache, idx, B: int, H: int, Dqk: int, Dv: int, k: int,
+                          softmax_scale: float, out, lse=None, ws=None, ws_bytes: int = 0,
+                          stream=None):
+    if ws is not None and not ws_bytes:
+        ws_bytes = ws.numel() * ws.element_size()
+    c = kv._c()
+    _check("dsa_sparse_mla_decode", lib().dsa_sparse_mla_decode(
+        dt, _ptr(q), ctypes.byref(c), _ptr(idx), B, H, Dqk, Dv, k, softmax_scale, _ptr(out),
+        _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dsa_sparse_mla_prefill(dt: int, q, kv, idx, T: int, H: int, Dqk: int, Dv: int, k: int,
+                           softmax_scale: float, out, lse=None, stream=None):
+    _check("dsa_sparse_mla_prefill", lib().dsa_sparse_mla_prefill(
+        dt, _ptr(q), _ptr(kv), _ptr(idx), T, H, Dqk, Dv, k, softmax_scale, _ptr(out), _ptr(lse),
+        _stream(stream)))

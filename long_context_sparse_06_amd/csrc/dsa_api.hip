@@ -1,0 +1,131 @@
+// C ABI of the DSA hot path (declared in include/dsa.h): host-side validation and
+// dispatch to the gfx950 kernels.  Nothing here allocates, frees or synchronises.
+#include "../../include/dsa.h"
+
+#include "kernels.h"
+
+namespace {
+
+dsa::CacheView view(const dsa_cache* c) {
+  return dsa::CacheView{c->data, c->scale, c->block_table, c->page_size, c->max_pages, c->seq_stride};
+}
+
+// Longest sequence a cache can hold; 0 if the descriptor is malformed.
+int64_t cache_capacity(const dsa_cache* c) {
+  if (c->block_table) {
+    if (c->page_size <= 0 || c->max_pages <= 0) return 0;
+    return (int64_t)c->page_size * c->max_pages;
+  }
+  return c->seq_stride > 0 ? c->seq_stride : 0;
+}
+
+dsa_status launched(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE";
+    case DSA_ERR_DTYPE: return "DSA_ERR_DTYPE";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+dsa_status dsa_index_scores(dsa_dtype dt, const void* q, const float* q_scale, const float* w,
+                            const dsa_cache* keys, const int32_t* row_seq, const int32_t* row_pos,
+                            int R, int H_I, int d_I, float* scores, int64_t ld, hipStream_t stream) {
+  if (!q || !w || !keys || !keys->data || !row_seq || !row_pos || !scores) return DSA_ERR_NULL;
+  if (dt != DSA_E4M3 && dt != DSA_F32) return DSA_ERR_DTYPE;
+  if (R <= 0 || H_I <= 0 || d_I <= 0 || R > 65535) return DSA_ERR_SHAPE;
+  const int64_t cap = cache_capacity(keys);
+  if (cap <= 0 || ld < cap) return DSA_ERR_SHAPE;
+  if ((int64_t)H_I * d_I > 16384) return DSA_ERR_UNSUPPORTED;
+  const dsa::CacheView kv = view(keys);
+  if (dt == DSA_E4M3 && H_I == 64 && d_I == 128)
+    return launched(dsa::launch_index_fp8_h64d128(static_cast<const uint8_t*>(q), q_scale, w, kv,
+                                                  row_seq, row_pos, R, cap, scores, ld, stream));
+  return launched(dsa::launch_index_generic(dt == DSA_E4M3, q, q_scale, w, kv, row_seq, row_pos, R,
+                                            H_I, d_I, cap, scores, ld, stream));
+}
+
+size_t dsa_topk_workspace_size(int R, int64_t ld, int k) {
+  if (R <= 0 || ld <= 0 || k <= 0) return 0;
+  return dsa::topk_workspace_bytes(R, ld, k);
+}
+
+dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
+                    int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!scores || !n_valid || !idx) return DSA_ERR_NULL;
+  if (R <= 0 || k <= 0 || ld <= 0 || k > 16384 || ld > (int64_t(1) << 24) || R > 2147483647 / 2)
+    return DSA_ERR_SHAPE;
+  const size_t need = dsa::topk_workspace_bytes(R, ld, k);
+  if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  return launched(dsa::launch_topk(scores, ld, n_valid, R, k, idx, ws, stream));
+}
+
+size_t dsa_sparse_mla_decode_workspace_size(int B, int H, int Dv, int k) {
+  if (B <= 0 || H <= 0 || Dv <= 0 || k <= 0) return 0;
+  return dsa::mla_decode_workspace_bytes(B, H, Dv, k);
+}
+
+static dsa_status mla_check(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx, int R,
+                            int H, int Dqk, int Dv, int k, void* out) {
+  if (!q || !kv || !idx || !out) return DSA_ERR_NULL;
+  if (dt != DSA_BF16 && dt != DSA_F32) return DSA_ERR_DTYPE;
+  if (R <= 0 || H <= 0 || Dqk <= 0 || Dv <= 0 || k <= 0 || Dv > Dqk) return DSA_ERR_SHAPE;
+  if ((int64_t)R * H > 2147483647LL) return DSA_ERR_SHAPE;
+  return DSA_OK;
+}
+
+static bool mla_fast(dsa_dtype dt, int H, int Dqk, int Dv) {
+  return dt == DSA_BF16 && Dqk == 576 && Dv == 512 && H % 64 == 0;
+}
+
+static dsa_status mla_generic_ok(int Dqk, int k) {
+  // logits of one (row, head) and the query row sit in LDS
+  return ((size_t)Dqk + k + 8) * sizeof(float) <= 64 * 1024 && Dqk <= 1024 ? DSA_OK : DSA_ERR_UNSUPPORTED;
+}
+
+dsa_status dsa_sparse_mla_decode(dsa_dtype dt, const void* q, const dsa_cache* kv, const int32_t* idx,
+                                 int B, int H, int Dqk, int Dv, int k, float softmax_scale, void* out,
+                                 float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!kv) return DSA_ERR_NULL;
+  dsa_status st = mla_check(dt, q, kv->data, idx, B, H, Dqk, Dv, k, out);
+  if (st != DSA_OK) return st;
+  if (cache_capacity(kv) <= 0) return DSA_ERR_SHAPE;
+  const dsa::CacheView v = view(kv);
+  if (mla_fast(dt, H, Dqk, Dv)) {
+    const size_t need = dsa::mla_decode_workspace_bytes(B, H, Dv, k);
+    if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+    return launched(dsa::launch_mla_bf16(static_cast<const uint16_t*>(q), v, idx, B, H, k, true,
+                                         softmax_scale, static_cast<uint16_t*>(out), lse, ws, ws_bytes,
+                                         stream));
+  }
+  if ((st = mla_generic_ok(Dqk, k)) != DSA_OK) return st;
+  return launched(dsa::launch_mla_generic(dt == DSA_BF16, q, v, idx, B, H, Dqk, Dv, k, true,
+                                          softmax_scale, out, lse, stream));
+}
+
+dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,
+                                  int T, int H, int Dqk, int Dv, int k, float softmax_scale, void* out,
+                                  float* lse, hipStream_t stream) {
+  dsa_status st = mla_check(dt, q, kv, idx, T, H, Dqk, Dv, k, out);
+  if (st != DSA_OK) return st;
+  const dsa::CacheView v{kv, nullptr, nullptr, 0, 0, (int64_t)T};
+  if (mla_fast(dt, H, Dqk, Dv))
+    return launched(dsa::launch_mla_bf16(static_cast<const uint16_t*>(q), v, idx, T, H, k, false,
+                                         softmax_scale, static_cast<uint16_t*>(out), lse, nullptr, 0,
+                                         stream));
+  if ((st = mla_generic_ok(Dqk, k)) != DSA_OK) return st;
+  return launched(dsa::launch_mla_generic(dt == DSA_BF16, q, v, idx, T, H, Dqk, Dv, k, false,
+                                          softmax_scale, out, lse, stream));
+}
+
+}  // extern "C"

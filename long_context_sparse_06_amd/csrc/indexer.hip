@@ -1,0 +1,186 @@
+// Lightning indexer: I[r,s] = k_scale[s] * q_scale[r] * sum_j w[r,j] * ReLU(q[r,j,:] . k[s,:]).
+//
+// The pages give the indexer only as the lightweight FP8 first tier of "FP8 index ->
+// top-k selection -> sparse core attention" (MarkTechPost, "DeepSeek V3.2-Exp Cuts
+// Long-Context Costs with DeepSeek Sparse Attention (DSA) ...") and as the "Lightning
+// Indexer" that computes lightweight index scores (maplevalley.com.cn news 1594152,
+// section 1); the ReLU-of-per-head-dots form above is this library's reading.
+//
+// Fast path (H_I = 64, d_I = 128, e4m3): one gfx950 v_mfma_scale_f32_16x16x128_f8f6f4
+// per 16 heads x 16 keys covers the whole 128-byte key row, so a key is read from HBM
+// exactly once and multiplied against all 64 query heads held in registers.  The
+// ReLU / w-weighted head sum / per-token scale run in fp32 in the MFMA result layout
+// (lane = key, 4 rows per lane) and two cross-lane adds finish the head sum.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kIdxWaves = 4;
+constexpr int kIdxUnroll = 4;  // 16-key groups per wave per loop trip
+
+template <bool PAGED>
+__global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ kdata, const float* __restrict__ kscale,
+    const int32_t* __restrict__ table, int max_pages, int page_size, int page_shift,
+    int64_t seq_stride, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
+    float* __restrict__ scores, int64_t ld, int keys_per_wg) {
+  const int r = blockIdx.x;
+  const int64_t n = (int64_t)row_pos[r] + 1;
+  const int64_t wg_begin = (int64_t)blockIdx.y * keys_per_wg;
+  if (wg_begin >= n) return;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = threadIdx.x / WAVE;
+  const int col = lane & 15;   // key (B column) / head row (A row) within a 16-tile
+  const int grp = lane >> 4;   // 32-byte k-slice of the 128-byte row
+  const int seq = row_seq[r];
+
+  // A operand: q[r, 16*ht + col, 32*grp .. 32*grp+31] (e4m3 bytes).
+  v8i qa[4];
+  const uint8_t* qr = q + (int64_t)r * (64 * 128);
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const uint4* p = reinterpret_cast<const uint4*>(qr + (16 * ht + col) * 128 + 32 * grp);
+    const uint4 a = p[0], b = p[1];
+    qa[ht] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  }
+  // Result rows held by this lane are heads 16*ht + 4*grp + i.
+  float wr[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const float4 v = *reinterpret_cast<const float4*>(w + (int64_t)r * 64 + 16 * ht + 4 * grp);
+    wr[ht][0] = v.x; wr[ht][1] = v.y; wr[ht][2] = v.z; wr[ht][3] = v.w;
+  }
+  const float qs = q_scale ? q_scale[r] : 1.0f;
+  const int per_wave = keys_per_wg / kIdxWaves;
+  const int64_t wbeg = wg_begin + (int64_t)wave * per_wave;
+  const int64_t wend = min(wbeg + per_wave, n);
+  float* srow = scores + (int64_t)r * ld;
+
+  for (int64_t s0 = wbeg; s0 < wend; s0 += 16 * kIdxUnroll) {
+    v8i kb[kIdxUnroll];
+    float ks[kIdxUnroll];
+#pragma unroll
+    for (int u = 0; u < kIdxUnroll; ++u) {
+      const int64_t s = min(s0 + 16 * u + col, n - 1);  // clamp: rows past n are never stored
+      int64_t row;
+      if (PAGED) {
+        const int64_t pg = page_shift >= 0 ? (s >> page_shift) : s / page_size;
+        const int64_t off = page_shift >= 0 ? (s & (page_size - 1)) : s % page_size;
+        row = (int64_t)table[(int64_t)seq * max_pages + pg] * page_size + off;
+      } else {
+        row = (int64_t)seq * seq_stride + s;
+      }
+      const uint4* p = reinterpret_cast<const uint4*>(kdata + row * 128 + 32 * grp);
+      const uint4 a = p[0];
+      const uint4 b = p[1];
+      kb[u] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+      ks[u] = kscale ? kscale[row] : 1.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kIdxUnroll; ++u) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // cbsz/blgp = 0: both operands OCP e4m3; scale exponent 127 = x1.
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb[u], acc, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum += wr[ht][i] * fmaxf(acc[i], 0.0f);
+      }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      const int64_t s = s0 + 16 * u + col;
+      if (grp == 0 && s < wend) srow[s] = sum * ks[u] * qs;
+    }
+  }
+}
+
+// Any H_I, d_I; fp32 or e4m3 operands.  One thread per key; the query row sits in LDS.
+template <bool FP8>
+__global__ __launch_bounds__(256) void index_generic_kernel(
+    const void* __restrict__ qv, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const void* __restrict__ kv, const float* __restrict__ kscale, const int32_t* __restrict__ table,
+    int max_pages, int page_size, int64_t seq_stride, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int HI, int dI, float* __restrict__ scores, int64_t ld) {
+  extern __shared__ float sq[];  // [HI*dI] query row, then [HI] weights
+  const int r = blockIdx.x;
+  const int64_t n = (int64_t)row_pos[r] + 1;
+  const int64_t base = (int64_t)blockIdx.y * blockDim.x;
+  if (base >= n) return;
+  for (int i = threadIdx.x; i < HI * dI; i += blockDim.x) {
+    const int64_t o = (int64_t)r * HI * dI + i;
+    sq[i] = FP8 ? e4m3_to_f32(static_cast<const uint8_t*>(qv)[o]) : static_cast<const float*>(qv)[o];
+  }
+  for (int j = threadIdx.x; j < HI; j += blockDim.x) sq[HI * dI + j] = w[(int64_t)r * HI + j];
+  __syncthreads();
+  const int64_t s = base + threadIdx.x;
+  if (s >= n) return;
+  const int seq = row_seq[r];
+  int64_t row;
+  if (table) {
+    row = (int64_t)table[(int64_t)seq * max_pages + s / page_size] * page_size + s % page_size;
+  } else {
+    row = (int64_t)seq * seq_stride + s;
+  }
+  float acc = 0.0f;
+  for (int j = 0; j < HI; ++j) {
+    float dot = 0.0f;
+    for (int d = 0; d < dI; ++d) {
+      const float kd = FP8 ? e4m3_to_f32(static_cast<const uint8_t*>(kv)[row * dI + d])
+                           : static_cast<const float*>(kv)[row * dI + d];
+      dot = fmaf(sq[j * dI + d], kd, dot);
+    }
+    acc = fmaf(sq[HI * dI + j], fmaxf(dot, 0.0f), acc);
+  }
+  const float ks = kscale ? kscale[row] : 1.0f;
+  const float qs = q_scale ? q_scale[r] : 1.0f;
+  scores[(int64_t)r * ld + s] = acc * ks * qs;
+}
+
+}  // namespace
+
+hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, const float* w,
+                                    const CacheView& keys, const int32_t* row_seq,
+                                    const int32_t* row_pos, int R, int64_t n_bound, float* scores,
+                                    int64_t ld, hipStream_t s) {
+  // Aim for ~2048 workgroups; at least 512 keys per workgroup to amortise the 8 KB q load.
+  const int64_t total = (int64_t)R * n_bound;
+  int64_t kpw = (total / 2048 + 255) / 256 * 256;
+  kpw = kpw < 512 ? 512 : (kpw > 4096 ? 4096 : kpw);
+  const dim3 grid((unsigned)R, (unsigned)((n_bound + kpw - 1) / kpw));
+  const uint8_t* kd = static_cast<const uint8_t*>(keys.data);
+  if (keys.table) {
+    const int ps = keys.page_size;
+    const int shift = (ps & (ps - 1)) == 0 ? __builtin_ctz(ps) : -1;
+    index_fp8_kernel<true><<<grid, kIdxWaves * WAVE, 0, s>>>(
+        q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
+        scores, ld, (int)kpw);
+  } else {
+    index_fp8_kernel<false><<<grid, kIdxWaves * WAVE, 0, s>>>(
+        q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, scores,
+        ld, (int)kpw);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index_generic(bool fp8, const void* q, const float* q_scale, const float* w,
+                                const CacheView& keys, const int32_t* row_seq, const int32_t* row_pos,
+                                int R, int HI, int dI, int64_t n_bound, float* scores, int64_t ld,
+                                hipStream_t s) {
+  const dim3 grid((unsigned)R, (unsigned)((n_bound + 255) / 256));
+  const size_t lds = sizeof(float) * ((size_t)HI * dI + HI);
+  if (fp8)
+    index_generic_kernel<true><<<grid, 256, lds, s>>>(q, q_scale, w, keys.data, keys.scale, keys.table,
+                                                      keys.max_pages, keys.page_size, keys.seq_stride,
+                                                      row_seq, row_pos, HI, dI, scores, ld);
+  else
+    index_generic_kernel<false><<<grid, 256, lds, s>>>(q, q_scale, w, keys.data, keys.scale, keys.table,
+                                                       keys.max_pages, keys.page_size, keys.seq_stride,
+                                                       row_seq, row_pos, HI, dI, scores, ld);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

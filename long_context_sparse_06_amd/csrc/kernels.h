@@ -1,0 +1,42 @@
+// Host-side launchers of the DSA kernels (internal; the public ABI is include/dsa.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct CacheView {
+  const void* data;
+  const float* scale;
+  const int32_t* table;
+  int page_size;
+  int max_pages;
+  int64_t seq_stride;
+};
+
+// ---- indexer
+hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, const float* w,
+                                    const CacheView& keys, const int32_t* row_seq,
+                                    const int32_t* row_pos, int R, int64_t n_bound, float* scores,
+                                    int64_t ld, hipStream_t s);
+hipError_t launch_index_generic(bool fp8, const void* q, const float* q_scale, const float* w,
+                                const CacheView& keys, const int32_t* row_seq, const int32_t* row_pos,
+                                int R, int HI, int dI, int64_t n_bound, float* scores, int64_t ld,
+                                hipStream_t s);
+
+// ---- top-k
+size_t topk_workspace_bytes(int R, int64_t ld, int k);
+hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
+                       int32_t* idx, void* ws, hipStream_t s);
+
+// ---- sparse MLA
+size_t mla_decode_workspace_bytes(int B, int H, int Dv, int k);
+hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t* idx, int R,
+                           int H, int k, bool decode, float scale, uint16_t* out, float* lse,
+                           void* ws, size_t ws_bytes, hipStream_t s);
+hipError_t launch_mla_generic(bool bf16, const void* q, const CacheView& kv, const int32_t* idx,
+                              int R, int H, int Dqk, int Dv, int k, bool decode, float scale,
+                              void* out, float* lse, hipStream_t s);
+
+}  // namespace dsa

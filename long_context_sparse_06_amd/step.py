@@ -1,0 +1,126 @@
+"""One DSA attention step composed from the three C-ABI calls.
+
+The pages' order -- "FP8 index -> top-k selection -> sparse core attention"
+(MarkTechPost, "DeepSeek V3.2-Exp Cuts Long-Context Costs with DeepSeek Sparse
+Attention (DSA) ...") -- run as dsa_index_scores -> dsa_topk -> dsa_sparse_mla_*.
+These classes only own the intermediate buffers (score rows, kept indices,
+workspaces, outputs; allocated once, at construction) and issue the calls in order.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (BF16, E4M3, F32, Cache, dsa_index_scores, dsa_sparse_mla_decode,
+               dsa_sparse_mla_decode_workspace_size, dsa_sparse_mla_prefill, dsa_topk,
+               dsa_topk_workspace_size)
+
+
+class DecodeStep:
+    """Decode for B sequences, one new token each (its KV already in the caches).
+
+    Inputs (device tensors): q_idx [B,H_I,d_I] e4m3 codes (uint8), q_scale [B], w [B,H_I],
+    key cache (+ per-token scale), q [B,H,Dqk] bf16, latent cache bf16, row_seq/row_pos/
+    n_valid [B] int32.  `ld` is the caches' capacity per sequence.
+    """
+
+    def __init__(self, *, q_idx, q_scale, w, keys, k_scale, q, kv, row_seq, row_pos, n_valid, ld,
+                 k, softmax_scale, Dv, block_table=None, page_size=0, seq_stride=0, fp32=False):
+        dev = q.device
+        self.B, self.H, self.Dqk = q.shape
+        self.Dv = int(Dv)
+        self.HI, self.dI = q_idx.shape[1], q_idx.shape[2]
+        self.k, self.ld, self.scale = int(k), int(ld), float(softmax_scale)
+        self.q_idx, self.q_scale, self.w, self.q = q_idx, q_scale, w, q
+        self.row_seq, self.row_pos, self.n_valid = row_seq, row_pos, n_valid
+        self.keys = Cache(keys, k_scale, block_table, page_size, seq_stride)
+        self.kv = Cache(kv, None, block_table, page_size, seq_stride)
+        self.idx_dt = F32 if fp32 else E4M3
+        self.mla_dt = F32 if fp32 else BF16
+        self.scores = torch.empty(self.B, self.ld, dtype=torch.float32, device=dev)
+        self.idx = torch.empty(self.B, self.k, dtype=torch.int32, device=dev)
+        tw = dsa_topk_workspace_size(self.B, self.ld, self.k)
+        self.topk_ws = torch.empty(max(tw, 1), dtype=torch.uint8, device=dev)
+        self.topk_ws_bytes = tw
+        odt = torch.float32 if fp32 else torch.bfloat16
+        self.out = torch.empty(self.B, self.H, self.Dv, dtype=odt, device=dev)
+        self.lse = torch.empty(self.B, self.H, dtype=torch.float32, device=dev)
+        mw = dsa_sparse_mla_decode_workspace_size(self.B, self.H, self.Dv, self.k)
+        self.mla_ws = torch.empty(max(mw, 1), dtype=torch.uint8, device=dev)
+        self.mla_ws_bytes = mw
+
+    @classmethod
+    def from_inputs(cls, d, k, softmax_scale, Dv, fp32=False):
+        """From an object carrying the device tensors by name (q_idx, q_scale, w, keys, k_scale,
+        q, kv, row_seq, row_pos, n_valid, block_table, page_size, seq_stride, ld)."""
+        return cls(q_idx=d.q_idx, q_scale=d.q_scale, w=d.w, keys=d.keys, k_scale=d.k_scale, q=d.q,
+                   kv=d.kv, row_seq=d.row_seq, row_pos=d.row_pos, n_valid=d.n_valid, ld=d.ld, k=k,
+                   softmax_scale=softmax_scale, Dv=Dv, block_table=d.block_table,
+                   page_size=d.page_size, seq_stride=d.seq_stride, fp32=fp32)
+
+    def index(self, stream=None):
+        dsa_index_scores(self.idx_dt, self.q_idx, self.q_scale, self.w, self.keys, self.row_seq,
+                         self.row_pos, self.B, self.HI, self.dI, self.scores, self.ld, stream)
+
+    def topk(self, stream=None):
+        dsa_topk(self.scores, self.ld, self.n_valid, self.B, self.k, self.idx, self.topk_ws,
+                 self.topk_ws_bytes, stream)
+
+    def attend(self, stream=None):
+        dsa_sparse_mla_decode(self.mla_dt, self.q, self.kv, self.idx, self.B, self.H, self.Dqk,
+                              self.Dv, self.k, self.scale, self.out, self.lse, self.mla_ws,
+                              self.mla_ws_bytes, stream)
+
+    def run(self, stream=None):
+        self.index(stream)
+        self.topk(stream)
+        self.attend(stream)
+        return self.out, self.lse, self.idx
+
+
+class Prefill:
+    """Causal prefill of one sequence of T tokens: row t scores tokens 0..t."""
+
+    @classmethod
+    def from_inputs(cls, d, k, softmax_scale, Dv):
+        return cls(q_idx=d.q_idx, q_scale=d.q_scale, w=d.w, keys=d.keys, k_scale=d.k_scale, q=d.q,
+                   kv=d.kv, row_seq=d.row_seq, row_pos=d.row_pos, n_valid=d.n_valid, k=k,
+                   softmax_scale=softmax_scale, Dv=Dv, fp32=d.fp32)
+
+    def __init__(self, *, q_idx, q_scale, w, keys, k_scale, q, kv, row_seq, row_pos, n_valid, k,
+                 softmax_scale, Dv, fp32=False):
+        dev = q.device
+        self.T, self.H, self.Dqk = q.shape
+        self.Dv = int(Dv)
+        self.HI, self.dI = q_idx.shape[1], q_idx.shape[2]
+        self.k, self.scale = int(k), float(softmax_scale)
+        self.q_idx, self.q_scale, self.w, self.q, self.kvt = q_idx, q_scale, w, q, kv
+        self.row_seq, self.row_pos, self.n_valid = row_seq, row_pos, n_valid
+        self.keys = Cache(keys, k_scale, None, 0, self.T)
+        self.idx_dt = F32 if fp32 else E4M3
+        self.mla_dt = F32 if fp32 else BF16
+        self.scores = torch.empty(self.T, self.T, dtype=torch.float32, device=dev)
+        self.idx = torch.empty(self.T, self.k, dtype=torch.int32, device=dev)
+        tw = dsa_topk_workspace_size(self.T, self.T, self.k)
+        self.topk_ws = torch.empty(max(tw, 1), dtype=torch.uint8, device=dev)
+        self.topk_ws_bytes = tw
+        odt = torch.float32 if fp32 else torch.bfloat16
+        self.out = torch.empty(self.T, self.H, self.Dv, dtype=odt, device=dev)
+        self.lse = torch.empty(self.T, self.H, dtype=torch.float32, device=dev)
+
+    def index(self, stream=None):
+        dsa_index_scores(self.idx_dt, self.q_idx, self.q_scale, self.w, self.keys, self.row_seq,
+                         self.row_pos, self.T, self.HI, self.dI, self.scores, self.T, stream)
+
+    def topk(self, stream=None):
+        dsa_topk(self.scores, self.T, self.n_valid, self.T, self.k, self.idx, self.topk_ws,
+                 self.topk_ws_bytes, stream)
+
+    def attend(self, stream=None):
+        dsa_sparse_mla_prefill(self.mla_dt, self.q, self.kvt, self.idx, self.T, self.H, self.Dqk,
+                               self.Dv, self.k, self.scale, self.out, self.lse, stream)
+
+    def run(self, stream=None):
+        self.index(stream)
+        self.topk(stream)
+        self.attend(stream)
+        return self.out, self.lse, self.idx

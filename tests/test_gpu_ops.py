@@ -1,0 +1,290 @@
+"""GPU parity of each C-ABI entry point against the CPU oracle (small, multi-tile shapes).
+
+Every case feeds both sides the same bytes; see tests/parity.py for the rules.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from datagen.device import tensor, upload_decode, upload_prefill
+from oracle import pipeline
+from oracle.formats import decode_bf16, decode_e4m3
+import parity
+
+pytestmark = pytest.mark.gpu
+
+FULL = datagen.FULL
+
+
+def _case(name):
+    print(f"[case] {name}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_sparse_06_amd as dsa
+    dsa.lib()  # fails loudly if the library is not built
+    return dsa
+
+
+# ----------------------------------------------------------------------------- indexer
+@pytest.mark.parametrize("paged", [False, True])
+def test_index_scores_fp8(paged):
+    import long_context_sparse_06_amd as dsa
+    _case(f"index_scores_fp8 paged={paged}")
+    lengths = np.array([1000, 4097, 77, 2048])
+    inp = datagen.make_decode(4, None, FULL, seed=21, lengths=lengths, paged=paged)
+    d = upload_decode(inp)
+    scores = torch.full((d.B, d.ld), float("nan"), device="cuda")
+    dsa.dsa_index_scores(dsa.E4M3, d.q_idx, d.q_scale, d.w,
+                         dsa.Cache(d.keys, d.k_scale, d.block_table, d.page_size, d.seq_stride),
+                         d.row_seq, d.row_pos, d.B, FULL.HI, FULL.dI, scores, d.ld)
+    got = scores.cpu().numpy()
+    for b in range(d.B):
+        L = int(lengths[b])
+        ref = pipeline.decode_scores(inp, b)
+        keys, ks = pipeline.decode_keys(inp, b)
+        ref_abs = parity.abs_scores(decode_e4m3(inp.q_idx[b]), float(inp.q_scale[b]), inp.w[b], keys, ks)
+        parity.check_scores(got[b, :L], ref, ref_abs, f"row {b}")
+        assert np.isnan(got[b, L:]).all(), "entries past n_valid must stay untouched"
+
+
+def test_index_scores_fp8_negative_weights_and_zero_query():
+    import long_context_sparse_06_amd as dsa
+    _case("index_scores_fp8 signs")
+    inp = datagen.make_decode(2, 600, FULL, seed=22)
+    inp.w[0] = -inp.w[0]
+    inp.q_idx[1] = 0
+    d = upload_decode(inp)
+    scores = torch.empty((2, d.ld), device="cuda")
+    dsa.dsa_index_scores(dsa.E4M3, d.q_idx, d.q_scale, d.w, dsa.Cache(d.keys, d.k_scale, seq_stride=d.seq_stride),
+                         d.row_seq, d.row_pos, 2, FULL.HI, FULL.dI, scores, d.ld)
+    got = scores.cpu().numpy()
+    ref0 = pipeline.decode_scores(inp, 0)
+    keys, ks = pipeline.decode_keys(inp, 0)
+    parity.check_scores(got[0], ref0, parity.abs_scores(decode_e4m3(inp.q_idx[0]), float(inp.q_scale[0]),
+                                                        inp.w[0], keys, ks))
+    assert (got[0] <= 0).all()
+    assert (got[1] == 0).all() and not np.signbit(got[1]).any()   # ReLU of 0 gives +0
+
+
+def test_index_scores_generic_fp32():
+    import long_context_sparse_06_amd as dsa
+    _case("index_scores fp32 generic")
+    inp = datagen.make_config(1, T=130)
+    d = upload_prefill(inp)
+    T = inp.T
+    scores = torch.full((T, T), float("nan"), device="cuda")
+    dsa.dsa_index_scores(dsa.F32, d.q_idx, None, d.w, dsa.Cache(d.keys, None, seq_stride=T), d.row_seq,
+                         d.row_pos, T, 2, 32, scores, T)
+    got = scores.cpu().numpy()
+    for t in range(T):
+        ref = pipeline.prefill_scores(inp, t)
+        ref_abs = parity.abs_scores(inp.q_idx[t], 1.0, inp.w[t], inp.keys[: t + 1], np.ones(t + 1))
+        parity.check_scores(got[t, : t + 1], ref, ref_abs, f"t={t}")
+
+
+# ----------------------------------------------------------------------------- top-k
+def _run_topk(scores_np, n_valid, k):
+    import long_context_sparse_06_amd as dsa
+    R, ld = scores_np.shape
+    s = tensor(scores_np.astype(np.float32))
+    nv = tensor(np.asarray(n_valid, dtype=np.int32))
+    idx = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    wsb = dsa.dsa_topk_workspace_size(R, ld, k)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_topk(s, ld, nv, R, k, idx, ws, wsb)
+    return idx.cpu().numpy()
+
+
+def _expect_topk(scores_np, n_valid, k, got):
+    for r in range(scores_np.shape[0]):
+        n = int(n_valid[r])
+        ref = oracle.topk(scores_np[r, :n].astype(np.float64), k)
+        exp = np.full(k, -1, dtype=np.int64)
+        exp[: len(ref)] = ref
+        assert np.array_equal(got[r], exp), f"row {r} (n={n}): first diff at {np.nonzero(got[r] != exp)[0][:5]}"
+
+
+def test_topk_lds_rows_exact():
+    _case("topk lds rows")
+    rng = np.random.default_rng(31)
+    ld, k = 9000, 2048
+    n_valid = [0, 1, 2047, 2048, 2049, 9000, 9000, 9000, 5000, 3000]
+    R = len(n_valid)
+    s = rng.standard_normal((R, ld)).astype(np.float32)
+    s[5] = np.round(s[5] * 4) / 4                          # heavy ties
+    s[6] = 1.5                                             # all equal
+    s[7, ::2] = -0.0; s[7, 1::2] = 0.0                     # signed zeros only
+    s[8] = rng.integers(0, 3, ld).astype(np.float32)       # three values
+    s[9] = -np.abs(s[9])
+    got = _run_topk(s, n_valid, k)
+    _expect_topk(s, n_valid, k, got)
+
+
+def test_topk_lds_row_max_and_small_k():
+    _case("topk lds 32768 rows, small k")
+    rng = np.random.default_rng(32)
+    ld = 32768
+    s = rng.standard_normal((3, ld)).astype(np.float32)
+    s[1] = np.floor(s[1] * 8)
+    for k in (1, 7, 2048):
+        got = _run_topk(s, [32768, 32768, 20000], k)
+        _expect_topk(s, [32768, 32768, 20000], k, got)
+
+
+def test_topk_long_rows_exact():
+    _case("topk long rows")
+    rng = np.random.default_rng(33)
+    ld, k = 131072, 2048
+    n_valid = [131072, 32769, 100000, 131072, 131072, 40000, 131072, 5000]
+    R = len(n_valid)
+    s = rng.standard_normal((R, ld)).astype(np.float32)
+    s[3] = 0.25                                            # tie storm: survivors overflow LDS
+    s[4] = np.round(s[4] * 2) / 2                          # coarse values: big tie at threshold
+    s[5] = np.linspace(-1, 1, ld, dtype=np.float32)        # sorted
+    s[6] = s[6] * 1e-3 + 7.0                               # narrow range, shared high bits
+    got = _run_topk(s, n_valid, k)
+    _expect_topk(s, n_valid, k, got)
+    got2 = _run_topk(s, n_valid, k)                        # workspace reuse, determinism
+    assert np.array_equal(got, got2)
+
+
+def test_topk_long_rows_sample_misses_survivors():
+    _case("topk long rows, sample threshold keeps fewer than k")
+    # 1000 of the evenly spaced sample positions hold the largest scores, so the sample
+    # threshold lets only those 1000 (< k) survive and the resolve must select from the
+    # full row instead.
+    rng = np.random.default_rng(34)
+    ld, k = 65536, 2048
+    s = rng.uniform(0, 1, (1, ld)).astype(np.float32)
+    sample = (np.arange(2048) * ld) // 2048
+    s[0, sample[:1000]] = 10.0
+    got = _run_topk(s, [ld], k)
+    _expect_topk(s, [ld], k, got)
+
+
+# ----------------------------------------------------------------------------- sparse MLA
+def _random_sets(rng, lengths, k, holes=True):
+    B = len(lengths)
+    idx = np.full((B, k), -1, dtype=np.int32)
+    for b, L in enumerate(lengths):
+        m = min(k, int(L))
+        sel = np.sort(rng.choice(int(L), size=m, replace=False)).astype(np.int32)
+        idx[b, :m] = sel
+        if holes and m > 10:
+            idx[b, rng.choice(m, size=m // 10, replace=False)] = -1   # -1 anywhere is ignored
+    return idx
+
+
+@pytest.mark.parametrize("paged,regime", [(False, "gaussian"), (False, "peaked"), (True, "peaked")])
+def test_sparse_mla_decode_bf16(paged, regime):
+    import long_context_sparse_06_amd as dsa
+    _case(f"sparse_mla_decode paged={paged} regime={regime}")
+    rng = np.random.default_rng(41)
+    lengths = np.array([3000, 700, 2048, 9000, 40])
+    B, k = len(lengths), 2048
+    inp = datagen.make_decode(B, None, FULL, seed=42, lengths=lengths, paged=paged, regime=regime)
+    d = upload_decode(inp)
+    idx = _random_sets(rng, lengths, k)
+    scale = 1.0 / math.sqrt(FULL.Dqk)
+    out = torch.empty((B, FULL.H, FULL.Dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, FULL.H), device="cuda")
+    wsb = dsa.dsa_sparse_mla_decode_workspace_size(B, FULL.H, FULL.Dv, k)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_sparse_mla_decode(dsa.BF16, d.q, dsa.Cache(d.kv, None, d.block_table, d.page_size, d.seq_stride),
+                              tensor(idx), B, FULL.H, FULL.Dqk, FULL.Dv, k, scale, out, lse, ws, wsb)
+    o = out.float().cpu().numpy(); l = lse.cpu().numpy()
+    for b in range(B):
+        o_ref, lse_ref = pipeline.decode_attention(inp, b, idx[b], scale)
+        parity.check_attention(o[b], l[b], o_ref, lse_ref, parity.BF16_ATOL, f"b={b}")
+        if regime == "peaked":
+            assert parity.rel_l2(o[b], o_ref) <= 1e-2
+
+
+def test_sparse_mla_empty_and_single():
+    import long_context_sparse_06_amd as dsa
+    _case("sparse_mla_decode empty/single sets")
+    inp = datagen.make_decode(3, 100, FULL, seed=43)
+    d = upload_decode(inp)
+    k = 64
+    idx = np.full((3, k), -1, dtype=np.int32)
+    idx[1, 17] = 5                         # exactly one row kept
+    idx[2, :] = np.arange(64)              # a full set
+    out = torch.empty((3, FULL.H, FULL.Dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((3, FULL.H), device="cuda")
+    wsb = dsa.dsa_sparse_mla_decode_workspace_size(3, FULL.H, FULL.Dv, k)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_sparse_mla_decode(dsa.BF16, d.q, dsa.Cache(d.kv, seq_stride=d.seq_stride), tensor(idx), 3, FULL.H,
+                              FULL.Dqk, FULL.Dv, k, 0.04, out, lse, ws, wsb)
+    o = out.float().cpu().numpy(); l = lse.cpu().numpy()
+    assert (o[0] == 0).all() and np.isneginf(l[0]).all()
+    v5 = decode_bf16(inp.kv[1, 5, : FULL.Dv])
+    assert np.array_equal(o[1], np.broadcast_to(v5, o[1].shape))      # softmax of one row = 1 exactly
+    o_ref, lse_ref = pipeline.decode_attention(inp, 1, idx[1], 0.04)
+    parity.check_attention(o[1], l[1], o_ref, lse_ref, parity.BF16_ATOL)
+    o_ref, lse_ref = pipeline.decode_attention(inp, 2, idx[2], 0.04)
+    parity.check_attention(o[2], l[2], o_ref, lse_ref, parity.BF16_ATOL)
+
+
+def test_sparse_mla_prefill_bf16():
+    import long_context_sparse_06_amd as dsa
+    _case("sparse_mla_prefill bf16")
+    rng = np.random.default_rng(44)
+    T, k = 300, 128
+    inp = datagen.make_prefill(T, FULL, seed=45)
+    d = upload_prefill(inp)
+    idx = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        m = min(k, t + 1)
+        idx[t, :m] = np.sort(rng.choice(t + 1, size=m, replace=False))
+    scale = 1.0 / math.sqrt(FULL.Dqk)
+    out = torch.empty((T, FULL.H, FULL.Dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, FULL.H), device="cuda")
+    dsa.dsa_sparse_mla_prefill(dsa.BF16, d.q, d.kv, tensor(idx), T, FULL.H, FULL.Dqk, FULL.Dv, k, scale, out, lse)
+    o = out.float().cpu().numpy(); l = lse.cpu().numpy()
+    for t in list(range(0, T, 7)) + [T - 1]:
+        o_ref, lse_ref = pipeline.prefill_attention(inp, t, idx[t], scale)
+        parity.check_attention(o[t], l[t], o_ref, lse_ref, parity.BF16_ATOL, f"t={t}")
+
+
+def test_sparse_mla_generic_fp32_decode():
+    import long_context_sparse_06_amd as dsa
+    _case("sparse_mla_decode fp32 generic")
+    rng = np.random.default_rng(46)
+    sh = datagen.TINY
+    B, L, k = 3, 200, 32
+    x = datagen.gaussian(rng, (B, sh.H, sh.Dqk))
+    kv = datagen.gaussian(rng, (B, L, sh.Dqk))
+    idx = _random_sets(rng, [L, 20, L], k)
+    out = torch.empty((B, sh.H, sh.Dv), device="cuda")
+    lse = torch.empty((B, sh.H), device="cuda")
+    dsa.dsa_sparse_mla_decode(dsa.F32, tensor(x), dsa.Cache(tensor(kv), seq_stride=L), tensor(idx), B, sh.H,
+                              sh.Dqk, sh.Dv, k, 0.11, out, lse)
+    o = out.cpu().numpy(); l = lse.cpu().numpy()
+    for b in range(B):
+        sel = idx[b][idx[b] >= 0]
+        o_ref, lse_ref = oracle.sparse_mla(x[b].astype(np.float64), kv[b, sel].astype(np.float64), sh.Dv, 0.11)
+        parity.check_attention(o[b], l[b], o_ref, lse_ref, parity.F32_ATOL, f"b={b}")
+
+
+def test_run_to_run_determinism():
+    import long_context_sparse_06_amd as dsa
+    from long_context_sparse_06_amd.step import DecodeStep
+    _case("determinism")
+    inp = datagen.make_decode(3, 6000, FULL, seed=47)
+    d = upload_decode(inp)
+    st = DecodeStep.from_inputs(d, 2048, 1 / 24, FULL.Dv)
+    a = [t.clone() for t in st.run()]
+    b = [t.clone() for t in st.run()]
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
