@@ -1,0 +1,209 @@
+"""Benchmark of one DSA decode step at 128k context on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+
+A step is the whole hot path for one new token per sequence: dsa_index_scores (FP8
+lightning indexer over every cached token) -> dsa_topk (k = 2048) -> dsa_sparse_mla_decode
+(MLA in MQA mode over the kept rows, split-KV combine included).  The default workload is
+batch 8 x 131072 context (128 query heads, 576-wide bf16 latent rows, 64 x 128 e4m3
+indexer), synthetic N(0,1)/sqrt(d) data (seed 1003).  Inputs are resident in HBM before
+timing starts; `--copies` distinct copies of the caches are rotated step by step so the
+256 MB Infinity Cache cannot serve a step from the previous one.  The step is captured
+once per copy in a HIP graph and replayed (the library never allocates or synchronises,
+so capture is plain); an eager pass of the same steps with HIP events around every
+indexer launch gives the indexer's average duration for the roofline figure.
+
+Prints one JSON line (rank 0, N = 1).  Multi-GPU runs are not part of this build.
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "DSA decode tokens/s & us/step at 128k ctx (indexer+top-k+sparse MLA); % roofline"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=3, choices=[2, 3, 5])
+    p.add_argument("--copies", type=int, default=4)
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import datagen
+    import long_context_sparse_06_amd as dsa
+    from datagen.device import upload_decode
+    from long_context_sparse_06_amd.step import DecodeStep
+
+    dsa.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = datagen.CONFIGS[args.config]
+    t0 = time.time()
+    inp = datagen.make_config(args.config)
+    log(f"[bench] generated {cfg['name']} in {time.time() - t0:.1f}s")
+    d0 = upload_decode(inp, dev)
+    sh = inp.shapes
+    scale = 1.0 / math.sqrt(sh.Dqk)
+    copies = [d0] + [dataclasses.replace(d0, keys=d0.keys.clone(), k_scale=d0.k_scale.clone(),
+                                         kv=d0.kv.clone()) for _ in range(1, args.copies)]
+    steps = [DecodeStep.from_inputs(c, sh.k, scale, sh.Dv) for c in copies]
+    torch.cuda.synchronize()
+    B = inp.B
+    L = inp.lengths.astype(np.int64)
+
+    # ---- algorithmic work (bytes the method must move), per step
+    idx_bytes = int(L.sum()) * (sh.dI + 4) + B * (sh.HI * sh.dI + 4 * sh.HI + 4)
+    kept = np.minimum(L, sh.k)
+    mla_bytes = int(kept.sum()) * (2 * sh.Dqk + 4) + B * sh.H * (2 * sh.Dqk + 2 * sh.Dv + 4)
+    table_bytes = 0 if inp.block_table is None else int(((L + inp.page_size - 1) // inp.page_size).sum()) * 4 * 2
+    step_bytes = idx_bytes + mla_bytes + table_bytes
+    roof_us = step_bytes / (HBM_PEAK_GBS * 1e3)
+
+    stream = torch.cuda.current_stream()
+    # ---- graphs (one per copy)
+    use_graph = not args.no_graph
+    graphs = []
+    if use_graph:
+        for st in steps:  # warm the kernels once before capture
+            st.run()
+        torch.cuda.synchronize()
+        for st in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                st.run()
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def one(i):
+        if use_graph:
+            graphs[i % len(steps)].replay()
+        else:
+            steps[i % len(steps)].run()
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # ---- eager pass with HIP events around each op (on the stream the kernels run on)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(min(args.warmup, 5)):
+        steps[i % len(steps)].run()
+    torch.cuda.synchronize()
+    te0 = time.perf_counter()
+    for i in range(args.steps):
+        st = steps[i % len(steps)]
+        e = ev[i]
+        e[0].record(stream)
+        st.index()
+        e[1].record(stream)
+        st.topk()
+        e[2].record(stream)
+        st.attend()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    te1 = time.perf_counter()
+    t_idx = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    t_topk = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    t_mla = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
+    idx_us = float(t_idx.mean())
+    achieved = idx_bytes / (idx_us * 1e3)  # GB/s
+
+    # ---- quick self-check of the timed path against the first copy's eager result
+    ok = True
+    if use_graph:
+        ref = [t.clone() for t in (steps[0].idx, steps[0].out)]
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        ok = torch.equal(ref[0], steps[0].idx) and torch.equal(ref[1].view(torch.int16), steps[0].out.view(torch.int16))
+
+    # ---- CPU oracle on this host (bounded sample of the same workload)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import pipeline
+        threads = os.cpu_count()
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            pass
+        tc0 = time.perf_counter()
+        done = 0
+        while True:  # whole sequences, repeated until the time budget is used
+            pipeline.decode_step(inp, scale, rows=[done % B])
+            done += 1
+            if time.perf_counter() - tc0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - tc0
+        cpu = {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"{done} sequence-steps of this workload (each a full {int(L.max())}-token "
+                         f"index scan, top-k and sparse MLA for one sequence), numpy fp64, {el:.1f} s"}
+
+    out = {
+        "metric": METRIC,
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "us_per_step": ms_per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3+bf16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "batch": B, "context": int(L.max()),
+                   "context_mean": float(L.mean()), "top_k": sh.k, "heads": sh.H,
+                   "latent": sh.Dqk, "value_dim": sh.Dv, "indexer_heads": sh.HI, "indexer_dim": sh.dI,
+                   "paged": inp.block_table is not None, "cache_copies": len(steps),
+                   "graph": use_graph, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": "index_fp8_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "alg_bytes_per_launch": idx_bytes},
+        "step_roofline": {"alg_bytes": step_bytes, "roof_us": roof_us,
+                          "frac": roof_us / (ms_per_step * 1e3)},
+        "breakdown_us": {"index": idx_us, "topk": float(t_topk.mean()), "sparse_mla": float(t_mla.mean()),
+                         "eager_step": (te1 - te0) * 1e6 / args.steps},
+        "graph_replay_matches_eager": bool(ok),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,17 +9,22 @@
 // Fast path (H_I = 64, d_I = 128, e4m3): one gfx950 v_mfma_scale_f32_16x16x128_f8f6f4
 // per 16 heads x 16 keys covers the whole 128-byte key row, so a key is read from HBM
 // exactly once and multiplied against all 64 query heads held in registers.  The
-// ReLU / w-weighted head sum / per-token scale run in fp32 in the MFMA result layout
-// (lane = key, 4 rows per lane) and two cross-lane adds finish the head sum.
+// ReLU / w-weighted head sum / per-token scale run in fp32 on the MFMA results.
 #include "common.h"
 #include "kernels.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kIdxWaves = 4;
-constexpr int kIdxUnroll = 4;  // 16-key groups per wave per loop trip
+constexpr int kIdxWaves = 8;
+constexpr int kIdxBatch = 64;  // keys per wave per loop trip: four 16-key MFMA column groups
 
+// Score of 64 keys per loop trip and wave.  Lane (col, grp) feeds key s0 + 16*u + col, bytes
+// 32*grp .. 32*grp+31, to the MFMA of column group u; the result layout leaves the lane with
+// 16 of the 64 heads of that key, which are ReLU'd, weighted and summed in-lane.  A two-stage
+// butterfly of gfx950 lane swaps (v_permlane32_swap, v_permlane16_swap) then adds the four
+// partial sums of each group and leaves group g's totals in lanes 16*g .. 16*g+15, so the 64
+// scores of the trip leave in one coalesced 256-byte store.
 template <bool PAGED>
 __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
@@ -27,15 +32,27 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     const int32_t* __restrict__ table, int max_pages, int page_size, int page_shift,
     int64_t seq_stride, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
     float* __restrict__ scores, int64_t ld, int keys_per_wg) {
+  extern __shared__ int spage[];  // paged: physical page of each logical page of this range
   const int r = blockIdx.x;
   const int64_t n = (int64_t)row_pos[r] + 1;
   const int64_t wg_begin = (int64_t)blockIdx.y * keys_per_wg;
   if (wg_begin >= n) return;
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int wave = threadIdx.x / WAVE;
-  const int col = lane & 15;   // key (B column) / head row (A row) within a 16-tile
-  const int grp = lane >> 4;   // 32-byte k-slice of the 128-byte row
+  const int64_t wg_end = min(wg_begin + keys_per_wg, n);
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wave = tid / WAVE;
+  const int col = lane & 15;  // key (B column) / head row (A row) within a 16-tile
+  const int grp = lane >> 4;  // 32-byte k-slice of the 128-byte row
   const int seq = row_seq[r];
+
+  int64_t p_first = 0;
+  if (PAGED) {
+    p_first = page_shift >= 0 ? (wg_begin >> page_shift) : wg_begin / page_size;
+    const int64_t p_last = page_shift >= 0 ? ((wg_end - 1) >> page_shift) : (wg_end - 1) / page_size;
+    const int np = (int)(p_last - p_first + 1);
+    for (int i = tid; i < np; i += kIdxWaves * WAVE) spage[i] = table[(int64_t)seq * max_pages + p_first + i];
+    __syncthreads();
+  }
 
   // A operand: q[r, 16*ht + col, 32*grp .. 32*grp+31] (e4m3 bytes).
   v8i qa[4];
@@ -59,28 +76,30 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
   const int64_t wend = min(wbeg + per_wave, n);
   float* srow = scores + (int64_t)r * ld;
 
-  for (int64_t s0 = wbeg; s0 < wend; s0 += 16 * kIdxUnroll) {
-    v8i kb[kIdxUnroll];
-    float ks[kIdxUnroll];
-#pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
-      const int64_t s = min(s0 + 16 * u + col, n - 1);  // clamp: rows past n are never stored
-      int64_t row;
-      if (PAGED) {
-        const int64_t pg = page_shift >= 0 ? (s >> page_shift) : s / page_size;
-        const int64_t off = page_shift >= 0 ? (s & (page_size - 1)) : s % page_size;
-        row = (int64_t)table[(int64_t)seq * max_pages + pg] * page_size + off;
-      } else {
-        row = (int64_t)seq * seq_stride + s;
-      }
-      const uint4* p = reinterpret_cast<const uint4*>(kdata + row * 128 + 32 * grp);
-      const uint4 a = p[0];
-      const uint4 b = p[1];
-      kb[u] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-      ks[u] = kscale ? kscale[row] : 1.0f;
+  auto row_of = [&](int64_t s) -> int64_t {
+    if (PAGED) {
+      const int64_t pg = page_shift >= 0 ? (s >> page_shift) : s / page_size;
+      const int64_t off = page_shift >= 0 ? (s & (page_size - 1)) : s % page_size;
+      return (int64_t)spage[pg - p_first] * page_size + off;
     }
+    return (int64_t)seq * seq_stride + s;
+  };
+
+  for (int64_t s0 = wbeg; s0 < wend; s0 += kIdxBatch) {
+    // Addresses are clamped to the last valid key instead of branching, so every load issues.
+    v8i kb[4];
 #pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = row_of(min(s0 + 16 * u + col, wend - 1));
+      const uint4* p = reinterpret_cast<const uint4*>(kdata + row * 128 + 32 * grp);
+      const uint4 a = p[0], b = p[1];
+      kb[u] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    }
+    const int64_t s_out = s0 + lane;  // the key whose score this lane writes
+    const float ks = kscale ? kscale[row_of(min(s_out, wend - 1))] : 1.0f;
+    float part[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       float sum = 0.0f;
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
@@ -88,13 +107,19 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
         // cbsz/blgp = 0: both operands OCP e4m3; scale exponent 127 = x1.
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb[u], acc, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sum += wr[ht][i] * fmaxf(acc[i], 0.0f);
+        for (int i = 0; i < 4; ++i) sum = fmaf(wr[ht][i], __builtin_amdgcn_fmed3f(acc[i], 0.0f, 3.0e38f), sum);
       }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      const int64_t s = s0 + 16 * u + col;
-      if (grp == 0 && s < wend) srow[s] = sum * ks[u] * qs;
+      part[u] = sum;
     }
+    // Stage 1 (lanes l, l^32): lower half keeps groups 0/1, upper half 2/3.
+    const v2i x02 = __builtin_amdgcn_permlane32_swap(__float_as_int(part[0]), __float_as_int(part[2]), false, false);
+    const v2i x13 = __builtin_amdgcn_permlane32_swap(__float_as_int(part[1]), __float_as_int(part[3]), false, false);
+    const float h02 = __int_as_float(x02[0]) + __int_as_float(x02[1]);
+    const float h13 = __int_as_float(x13[0]) + __int_as_float(x13[1]);
+    // Stage 2 (rows of 16 lanes, r and r^1): row g ends with group g's full sum.
+    const v2i y = __builtin_amdgcn_permlane16_swap(__float_as_int(h02), __float_as_int(h13), false, false);
+    const float tot = __int_as_float(y[0]) + __int_as_float(y[1]);
+    if (s_out < wend) srow[s_out] = tot * ks * qs;
   }
 }
 
@@ -146,16 +171,18 @@ hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, cons
                                     const CacheView& keys, const int32_t* row_seq,
                                     const int32_t* row_pos, int R, int64_t n_bound, float* scores,
                                     int64_t ld, hipStream_t s) {
-  // Aim for ~2048 workgroups; at least 512 keys per workgroup to amortise the 8 KB q load.
+  // ~512 workgroups of 8 waves (two per CU at this kernel's register use); each wave's
+  // share is a multiple of the 64-key trip.
   const int64_t total = (int64_t)R * n_bound;
-  int64_t kpw = (total / 2048 + 255) / 256 * 256;
-  kpw = kpw < 512 ? 512 : (kpw > 4096 ? 4096 : kpw);
+  int64_t kpw = 512;
+  while (kpw < 4096 && total / (kpw * 2) >= 512) kpw *= 2;
   const dim3 grid((unsigned)R, (unsigned)((n_bound + kpw - 1) / kpw));
   const uint8_t* kd = static_cast<const uint8_t*>(keys.data);
   if (keys.table) {
     const int ps = keys.page_size;
     const int shift = (ps & (ps - 1)) == 0 ? __builtin_ctz(ps) : -1;
-    index_fp8_kernel<true><<<grid, kIdxWaves * WAVE, 0, s>>>(
+    const size_t lds = sizeof(int) * (size_t)(kpw / ps + 2);
+    index_fp8_kernel<true><<<grid, kIdxWaves * WAVE, lds, s>>>(
         q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
         scores, ld, (int)kpw);
   } else {

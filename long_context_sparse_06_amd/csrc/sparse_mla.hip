@@ -28,20 +28,47 @@ namespace {
 
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
-constexpr int kTok = 32;                       // rows per LDS tile
-constexpr int kRowChunks = kDqk * 2 / 16;      // 72 16-byte chunks per latent row
-constexpr int kRS = kDqk * 2 + 16;             // padded LDS row stride (bytes)
-constexpr int kTileBytes = kTok * kRS;
-constexpr int kMlaWaves = 4;
-constexpr int kMlaThreads = kMlaWaves * WAVE;
+constexpr int kTok = 32;                        // rows per LDS tile
+constexpr int kRowChunks = kDqk * 2 / 16;       // 72 16-byte chunks per latent row
+constexpr int kDmaPerTile = kRowChunks / 2;     // 36 wave-wide 1 KB copies per tile
+// Tile layout (chunk-major): copy j fills block j with chunk j of rows 0..31 (lanes 0-31)
+// and chunk j + 36 (lanes 32-63), 16 bytes per lane.  Blocks are 1088 bytes apart so
+// chunks 2d and 2d+1 (one 16-column value slice) sit 16 banks apart for the transposing
+// reads; a 16-lane read of one chunk covers 256 contiguous bytes (all 64 banks).
+constexpr int kBlock = 1024 + 64;
+constexpr int kBufBytes = kDmaPerTile * kBlock;  // 39168
+constexpr int kNBuf = 3;                        // ring depth: two tiles in flight during compute
+constexpr int kMlaWaves = 4;                    // compute waves, 16 heads each
+constexpr int kMlaThreads = (kMlaWaves + 1) * WAVE;          // + one loader wave
 constexpr int kHeadsPerWg = 16 * kMlaWaves;
-constexpr int kPrefetch = (kTok * kRowChunks + kMlaThreads - 1) / kMlaThreads;
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// Byte offset of (row, 16-byte chunk c) inside a tile.
+__device__ __forceinline__ int tile_off(int row, int c) {
+  return (c < kDmaPerTile ? c * kBlock : (c - kDmaPerTile) * kBlock + 512) + row * 16;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ v4bf lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(p));
 }
 
+// s_waitcnt with only the vector-memory counter constrained (expcnt, lgkmcnt left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__shared__ __attribute__((aligned(16))) char g_ring[kNBuf][kBufBytes];
+
+// One workgroup = (row r, 64 heads, a range of the kept set).  Wave 4 is the loader: it
+// streams each 32-row tile straight from global memory into a 3-deep LDS ring with
+// global_load_lds_dwordx4 (a row is gathered once and shared by all 64 heads) and never
+// reads the ring, so its copies stay in flight across the tile barriers; waves 0-3
+// compute.  The loader's only LDS reads are the row list `srow`, a different LDS array,
+// which keeps the compiler from waiting on the copies before them.
 template <bool PAGED, bool SPLIT>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -49,8 +76,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     const int32_t* __restrict__ idx, int k, int H, int decode, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml, int n_split, int tok_per_split) {
-  __shared__ __attribute__((aligned(16))) char tile[2][kTileBytes];
-  __shared__ int tidx[2][kTok];
+  extern __shared__ int srow[];  // [tok_per_split] cache row of each kept token, -1 = none
 
   const int HG = H / kHeadsPerWg;
   int bid = blockIdx.x;
@@ -60,81 +86,98 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   const int r = bid / HG;
   const int t_begin = sp * tok_per_split;
   const int t_end = min(k, t_begin + tok_per_split);
+  const int n_tok = t_end > t_begin ? t_end - t_begin : 0;
   const int seq = decode ? r : 0;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int32_t* irow = idx + (int64_t)r * k + t_begin;
+  // Rows are addressed relative to `base`: the sequence's first row (contiguous) or the
+  // pool (paged: the page table is resolved here, once per kept token).
+  const uint16_t* base = PAGED ? kv : kv + (int64_t)seq * seq_stride * kDqk;
+  // Query fragments of the compute waves, issued before the row list is built so the two
+  // latencies overlap: B[k = dim][n = head col] = q[r, h, 32*kk + 8*grp + j].
   const int col = lane & 15, grp = lane >> 4;
-  const int h = hg * kHeadsPerWg + 16 * w + col;
-  const int32_t* irow = idx + (int64_t)r * k;
-
-  // Query fragments: B[k = dim][n = head col] = q[r, h, 32*kk + 8*grp + j].
+  const int h = hg * kHeadsPerWg + 16 * min(w, kMlaWaves - 1) + col;
+  const uint16_t* qrow = q + ((int64_t)r * H + h) * kDqk;
   v8bf qf[kDqk / 32];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * kDqk + 8 * grp);
+  if (w < kMlaWaves) {
+    const uint4* qp = reinterpret_cast<const uint4*>(qrow + 8 * grp);
 #pragma unroll
     for (int kk = 0; kk < kDqk / 32; ++kk) {
       const uint4 x = qp[4 * kk];
       qf[kk] = __builtin_bit_cast(v8bf, x);
     }
   }
+  {
+    constexpr int U = 8;  // ids (and their page-table entries) read in batches
+    for (int i0 = 0; i0 < n_tok; i0 += U * kMlaThreads) {
+      int id[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kMlaThreads + tid;
+        const int v = irow[min(i, n_tok - 1)];  // unconditional load: no wait between batch members
+        id[u] = i < n_tok ? v : -1;
+      }
+      if (PAGED) {
+        int pg[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          pg[u] = table[(int64_t)seq * max_pages + (id[u] >= 0 ? id[u] : 0) / page_size];
+#pragma unroll
+        for (int u = 0; u < U; ++u) id[u] = id[u] >= 0 ? pg[u] * page_size + id[u] % page_size : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kMlaThreads + tid;
+        if (i < n_tok) srow[i] = id[u] >= 0 ? id[u] : -1;
+      }
+    }
+  }
+  __syncthreads();
+  const int ntiles = (n_tok + kTok - 1) / kTok;
 
+  if (w == kMlaWaves) {
+    // ---------------------------------------------------------------- loader wave
+    // Dead rows (past the range or index -1) copy this row's first query row, which is
+    // finite, so masked tokens never inject NaN into the value products.
+    const uint16_t* dummy = q + (int64_t)r * H * kDqk;
+    const int half = lane >> 5;  // lanes 32-63 copy the row's second half (chunks 36..71)
+    auto issue = [&](int t) {
+      char* dst = g_ring[t % kNBuf];
+      const int tok = t * kTok + (lane & 31);
+      const int row = tok < n_tok ? srow[tok] : -1;
+      const uint16_t* src = (row >= 0 ? base + (int64_t)row * kDqk : dummy) + half * (kDqk / 2);
+#pragma unroll
+      for (int j = 0; j < kDmaPerTile; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 8 * j), (lds_void*)(dst + j * kBlock), 16, 0, 0);
+    };
+    if (ntiles > 0) issue(0);
+    if (ntiles > 1) issue(1);
+    for (int t = 0; t < ntiles; ++t) {
+      if (t + 1 < ntiles) wait_vmcnt<kDmaPerTile>();  // tile t landed, t+1 may be in flight
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();                    // hand tile t to the compute waves
+      if (t + 2 < ntiles) issue(t + 2);                // its buffer was freed by tile t-1
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------------ compute waves
   v4f acc_o[kDv / 16];
 #pragma unroll
   for (int dt = 0; dt < kDv / 16; ++dt) acc_o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of scaled logits (log2 domain), per head = col
+  float m_run = -INFINITY;  // reference max of scaled logits (log2 domain), per head = col
   float l_run = 0.0f;       // this lane's share of the running sum
 
-  const int ntiles = t_end > t_begin ? (t_end - t_begin + kTok - 1) / kTok : 0;
-  uint4 pre[kPrefetch];
-  int pre_id = -1;
-
-  auto row_ptr = [&](int id) -> const uint16_t* {
-    int64_t row;
-    if (PAGED) {
-      row = (int64_t)table[(int64_t)seq * max_pages + id / page_size] * page_size + id % page_size;
-    } else {
-      row = (int64_t)seq * seq_stride + id;
-    }
-    return kv + row * kDqk;
-  };
-  auto prefetch = [&](int t0) {
-#pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) {
-      const int c = tid + i * kMlaThreads;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < kTok * kRowChunks) {
-        const int j = c / kRowChunks, ch = c % kRowChunks;
-        const int t = t0 + j;
-        const int id = t < t_end ? irow[t] : -1;
-        if (id >= 0) v = *reinterpret_cast<const uint4*>(row_ptr(id) + 8 * ch);
-      }
-      pre[i] = v;
-    }
-    pre_id = (tid < kTok && t0 + tid < t_end) ? irow[t0 + tid] : -1;
-  };
-
-  if (ntiles > 0) prefetch(t_begin);
-  for (int it = 0; it < ntiles; ++it) {
-    const int b = it & 1;
-    char* tb = tile[b];
-#pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) {
-      const int c = tid + i * kMlaThreads;
-      if (c < kTok * kRowChunks) {
-        const int j = c / kRowChunks, ch = c % kRowChunks;
-        *reinterpret_cast<uint4*>(tb + j * kRS + 16 * ch) = pre[i];
-      }
-    }
-    if (tid < kTok) tidx[b][tid] = pre_id;
-    __syncthreads();
-    if (it + 1 < ntiles) prefetch(t_begin + (it + 1) * kTok);
-
+  for (int t = 0; t < ntiles; ++t) {
+    __builtin_amdgcn_s_barrier();  // tile t is in g_ring[t % kNBuf]
+    const char* tb = g_ring[t % kNBuf];
     // ---- S^T = K Q^T for tokens 0..15 (st = 0) and 16..31 (st = 1)
     v4f acc_s[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kk = 0; kk < kDqk / 32; ++kk) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const v8bf a = *reinterpret_cast<const v8bf*>(tb + (16 * st + col) * kRS + 64 * kk + 16 * grp);
+        const v8bf a = *reinterpret_cast<const v8bf*>(tb + tile_off(16 * st + col, 4 * kk + grp));
         acc_s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], acc_s[st], 0, 0, 0);
       }
     }
@@ -145,16 +188,27 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = tidx[b][16 * st + 4 * grp + i] >= 0;
+        const int tok = t * kTok + 16 * st + 4 * grp + i;
+        const bool ok = tok < n_tok && srow[tok] >= 0;
         s[st][i] = ok ? acc_s[st][i] * scale_log2 : -INFINITY;
         mx = fmaxf(mx, s[st][i]);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // no valid token yet: p = 0
-    const float alpha = exp2f(m_run - m_use);               // m_run = -inf -> 0
+    // Lazy rescaling: the reference max only moves when a logit exceeds it by more than
+    // 2^8 (or on the first valid tile), so p <= 256 and the accumulators rarely rescale.
+    float m_ref = m_run;
+    if (__ballot(mx > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < kDv / 16; ++dt) acc_o[dt] *= alpha;
+      m_ref = m_new;
+    }
+    m_run = m_ref;
+    const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;  // no valid token yet: p = 0
     float p[2][4];
     float psum = 0.0f;
 #pragma unroll
@@ -165,12 +219,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
         psum += p[st][i];
       }
     }
-    l_run = l_run * alpha + psum;
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < kDv / 16; ++dt) acc_o[dt] *= alpha;
-    }
-    m_run = m_new;
+    l_run += psum;
     // P^T fragment: k-slot 8*grp + j <-> token 4*grp + j (j < 4) or 16 + 4*grp + (j - 4).
     v8bf pf;
 #pragma unroll
@@ -179,12 +228,15 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
       pf[4 + i] = (__bf16)p[1][i];
     }
     // ---- O^T += V^T P^T, 32 tiles of 16 value columns
-    const char* v0 = tb + (4 * grp + (col >> 2)) * kRS + 8 * (col & 3);
-    const char* v1 = v0 + 16 * kRS;
+    // lane (col, grp) of a transposing read supplies row 4*grp + col/4 (+16), value columns
+    // 16*dt + 4*(col&3) .. +3: chunk 2*dt + (col&3)/2, byte 8*(col&1) within it.
+    const int vrow = 4 * grp + (col >> 2);
+    const int vsub = 8 * (col & 1);
 #pragma unroll
     for (int dt = 0; dt < kDv / 16; ++dt) {
-      const v4bf lo = lds_read_tr16(v0 + 32 * dt);
-      const v4bf hi = lds_read_tr16(v1 + 32 * dt);
+      const int c = 2 * dt + ((col & 3) >> 1);
+      const v4bf lo = lds_read_tr16(tb + tile_off(vrow, c) + vsub);
+      const v4bf hi = lds_read_tr16(tb + tile_off(vrow + 16, c) + vsub);
       const v8bf a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, acc_o[dt], 0, 0, 0);
     }
@@ -226,25 +278,27 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
   if (pair >= RH) return;
   const int r = pair / H, h = pair % H;
   const int lane = threadIdx.x & (WAVE - 1);
+  const int64_t p0 = (int64_t)r * n_split * H + h;  // partial of split s at p0 + s * H
+  // Pass 1 reads only the (max, sum) pairs; pass 2 issues every split's value loads at
+  // once with its weight computed up front (no load depends on another).
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < n_split; ++s) {
-    const int64_t pr = ((int64_t)r * n_split + s) * H + h;
-    if (part_ml[2 * pr + 1] > 0.0f) M = fmaxf(M, part_ml[2 * pr]);
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * (p0 + (int64_t)s * H));
+    M = ml.y > 0.0f ? fmaxf(M, ml.x) : M;
   }
   float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float L = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const int64_t pr = ((int64_t)r * n_split + s) * H + h;
-      const float ls = part_ml[2 * pr + 1];
-      if (!(ls > 0.0f)) continue;
-      const float f = exp2f(part_ml[2 * pr] - M);
-      L += ls * f;
-      const float4* po = reinterpret_cast<const float4*>(part_o + pr * kDv + 8 * lane);
-      const float4 a = po[0], b = po[1];
-      o[0] += a.x * f; o[1] += a.y * f; o[2] += a.z * f; o[3] += a.w * f;
-      o[4] += b.x * f; o[5] += b.y * f; o[6] += b.z * f; o[7] += b.w * f;
-    }
+#pragma unroll 8
+  for (int s = 0; s < n_split; ++s) {
+    const int64_t pr = p0 + (int64_t)s * H;
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
+    const float f = (ml.y > 0.0f && M != -INFINITY) ? exp2f(ml.x - M) : 0.0f;
+    L += ml.y > 0.0f ? ml.y * f : 0.0f;
+    const float4* po = reinterpret_cast<const float4*>(part_o + pr * kDv + 8 * lane);
+    const float4 a = po[0], b = po[1];
+    o[0] += a.x * f; o[1] += a.y * f; o[2] += a.z * f; o[3] += a.w * f;
+    o[4] += b.x * f; o[5] += b.y * f; o[6] += b.z * f; o[7] += b.w * f;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   uint32_t pk[4];
@@ -325,11 +379,11 @@ struct SplitPlan {
 };
 
 SplitPlan split_plan(int B, int H, int k) {
-  // Enough workgroups to cover the chip twice, but at least 256 kept rows per workgroup
-  // so the partial (o, m, l) traffic stays below the gathered KV bytes.
+  // One workgroup per CU (the LDS ring allows no second one): split each sequence's kept
+  // set until ~256 workgroups exist, keeping at least 4 tiles (128 rows) per workgroup.
   const int groups = B * (H / kHeadsPerWg);
-  int ns = (512 + groups - 1) / groups;
-  const int max_ns = (k + 255) / 256;
+  int ns = (256 + groups - 1) / groups;
+  const int max_ns = (k + 4 * kTok - 1) / (4 * kTok);
   ns = ns < 1 ? 1 : (ns > max_ns ? max_ns : ns);
   int tps = (k + ns - 1) / ns;
   tps = (tps + kTok - 1) / kTok * kTok;
@@ -360,7 +414,7 @@ hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o ? part_o + (size_t)R * p.n_split * H * kDv : nullptr;
 #define DSA_MLA_LAUNCH(PG, SP)                                                                   \
-  mla_bf16_kernel<PG, SP><<<grid, kMlaThreads, 0, s>>>(q, kvp, kv.table, kv.max_pages,             \
+  mla_bf16_kernel<PG, SP><<<grid, kMlaThreads, sizeof(int) * p.tok_per_split, s>>>(q, kvp, kv.table, kv.max_pages,             \
                                                         kv.page_size, kv.seq_stride, idx, k, H,     \
                                                         decode ? 1 : 0, scale_log2, out, lse,       \
                                                         part_o, part_ml, p.n_split, p.tok_per_split)

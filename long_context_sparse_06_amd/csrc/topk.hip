@@ -14,12 +14,13 @@
 // to T are taken lowest index first and the output comes out sorted.
 //
 // Rows up to kRowMax scores are selected by one workgroup entirely in LDS.  Longer rows
-// (decode at 128k context) take two launches: one workgroup per row draws an evenly
-// spaced sample and sets a threshold theta whose expected survivor count is ~2k; then
-// many workgroups per row compact the survivors (in index order) and the last one to
-// finish resolves the exact top-k among them in LDS.  Correctness never depends on the
-// sample: if fewer than k or more than fit in LDS survive, that last workgroup selects
-// from the full row in global memory instead.
+// (decode at 128k context) take three launches: one workgroup per row draws an evenly
+// spaced sample and sets a threshold theta whose expected survivor count is ~2k; many
+// workgroups per row compact the survivors (in index order); one workgroup per row then
+// resolves the exact top-k among them in LDS.  The hand-offs are kernel boundaries: an
+// in-kernel device-scope fence costs a whole-L2 writeback and invalidate on this chip.
+// Correctness never depends on the sample: if fewer than k or more than fit in LDS
+// survive, the resolve selects from the full row in global memory instead.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,11 +33,12 @@ constexpr int kChunk = 4096;       // scores per workgroup in the long-row compa
 constexpr int kCandCap = 12288;    // survivors resolvable in LDS (96 KiB of key/index pairs)
 constexpr int kHistBins = 2048;    // 11-bit digits
 constexpr int kRowThreads = 1024;
-constexpr int kLongThreads = 256;
+constexpr int kLongThreads = 256;    // compaction workgroups
+constexpr int kResolveThreads = 1024;
 
 struct RowHeader {
-  uint32_t theta;
-  uint32_t done;
+  uint32_t theta;  // sample threshold key of a long row
+  uint32_t pad;
 };
 
 struct SelState {
@@ -66,6 +68,26 @@ struct GlobalRow {  // a score row in global memory
   __device__ uint32_t key(int i) const { return float_key(row[i]); }
   __device__ int id(int i) const { return i; }
 };
+
+// Visits elements i = tid, tid + NT, ... of [0, m) in batches of U per thread: all U keys of a
+// batch are read before any is used, so global-memory sources have U loads in flight
+// instead of one round trip per element.
+template <int NT, int U, class Src, class F>
+__device__ __forceinline__ void for_each_key(const Src& src, int m, F&& f) {
+  for (int base = 0; base < m; base += NT * U) {
+    uint32_t kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * NT + (int)threadIdx.x;
+      kv[u] = src.key(min(i, m - 1));  // unconditional: the batch's loads issue back to back
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * NT + (int)threadIdx.x;
+      if (i < m) f(i, kv[u]);
+    }
+  }
+}
 
 template <int NT>
 __device__ int block_excl_scan(int x, int* tmp) {
@@ -100,11 +122,10 @@ template <int NT, class Src>
 __device__ void find_threshold(const Src& src, int m, int k, int* hist, SelState& st, int* tmp) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
-  for (int i = tid; i < m; i += NT) {
-    const uint32_t key = src.key(i);
+  for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
     lmn = min(lmn, key);
     lmx = max(lmx, key);
-  }
+  });
   lmn = umin_wave(lmn);
   lmx = umax_wave(lmx);
   if (lane == 0) {
@@ -122,23 +143,24 @@ __device__ void find_threshold(const Src& src, int m, int k, int* hist, SelState
     st.mx = b;
   }
   __syncthreads();
-  const uint32_t mn = st.mn, mx = st.mx;
-  int shift = (mn == mx) ? 0 : 32 - __builtin_clz(mn ^ mx);  // bits below the common prefix
-  uint32_t prefix = shift == 32 ? 0u : (mx & ~((1u << shift) - 1u));
+  // Range-relative digits: the threshold lies in the key interval [lo, hi]; each pass
+  // splits that interval into at most 2048 equal bins of 2^s keys (s chosen from its
+  // width), so the histogram resolves wherever the keys actually are, in at most three
+  // passes for 32-bit keys.
+  uint32_t lo = st.mn;
+  const uint32_t hi0 = st.mx;
+  uint32_t hi = hi0;
   int need = k;
   bool exact = false;
-  while (shift > 0) {
-    const int bits = shift < 11 ? shift : 11;
-    shift -= bits;
-    const int nb = 1 << bits;
+  while (hi != lo) {
+    const uint32_t width = hi - lo;
+    const int s = max(0, 32 - __builtin_clz(width) - 11);
+    const int nb = (int)(width >> s) + 1;
     for (int i = tid; i < nb; i += NT) hist[i] = 0;
     __syncthreads();
-    const int hi = shift + bits;  // elements must match prefix above bit hi
-    for (int i = tid; i < m; i += NT) {
-      const uint32_t key = src.key(i);
-      const bool match = hi >= 32 || ((key >> hi) == (prefix >> hi));
-      if (match) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1);
-    }
+    for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
+      if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> s], 1);
+    });
     __syncthreads();
     // Thread t owns the t-th group of bins counted from the top.
     constexpr int kPer = (kHistBins + NT - 1) / NT;
@@ -162,16 +184,18 @@ __device__ void find_threshold(const Src& src, int m, int k, int* hist, SelState
     __syncthreads();
     const int d = st.digit;
     need -= st.above;
-    prefix |= (uint32_t)d << shift;
     const int cnt = hist[d];
+    const uint32_t new_lo = lo + ((uint32_t)d << s);
+    const uint64_t top = (uint64_t)new_lo + ((uint64_t)1 << s) - 1;
+    hi = top < (uint64_t)hi ? (uint32_t)top : hi;
+    lo = new_lo;
     __syncthreads();
-    if (cnt == need) {
+    if (cnt == need) {  // every key of the bin is taken: the selection is { key >= lo }
       exact = true;
       break;
     }
   }
-  // Not exact: prefix is now the full threshold key and `need` of the elements equal to
-  // it are taken (lowest index first).
+  const uint32_t prefix = lo;
   if (tid == 0) {
     st.T = prefix;
     st.need = need;
@@ -191,17 +215,25 @@ __device__ void emit_selected(const Src& src, int m, SelState& st, int32_t* __re
   const int per = ((m + NW - 1) / NW + WAVE - 1) / WAVE * WAVE;
   const int beg = w * per;
   const int end = min(m, beg + per);
-  int cgt = 0, ceq = 0;
-  for (int i = beg; i < end; i += WAVE) {
-    const int e = i + lane;
-    bool gt = false, eq = false;
-    if (e < end) {
-      const uint32_t key = src.key(e);
-      gt = exact ? key >= T : key > T;
-      eq = !exact && key == T;
+  constexpr int U = 8;  // rounds of 64 whose keys are read before they are used
+  auto keys_of = [&](int i0, uint32_t (&kv)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = i0 + u * WAVE + lane;
+      kv[u] = src.key(min(e, end - 1));
     }
-    cgt += __popcll(ballot(gt));
-    ceq += __popcll(ballot(eq));
+  };
+  int cgt = 0, ceq = 0;
+  for (int i0 = beg; i0 < end; i0 += U * WAVE) {
+    uint32_t kv[U];
+    keys_of(i0, kv);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = i0 + u * WAVE + lane;
+      const bool in = e < end;
+      cgt += __popcll(ballot(in && (exact ? kv[u] >= T : kv[u] > T)));
+      ceq += __popcll(ballot(in && !exact && kv[u] == T));
+    }
   }
   if (lane == 0) {
     st.wtot[0][w] = cgt;
@@ -217,20 +249,22 @@ __device__ void emit_selected(const Src& src, int m, SelState& st, int32_t* __re
     eq_before += e_v;
   }
   int eq_run = 0, sel_run = 0;
-  for (int i = beg; i < end; i += WAVE) {
-    const int e = i + lane;
-    bool gt = false, eq = false;
-    if (e < end) {
-      const uint32_t key = src.key(e);
-      gt = exact ? key >= T : key > T;
-      eq = !exact && key == T;
+  for (int i0 = beg; i0 < end; i0 += U * WAVE) {
+    uint32_t kv[U];
+    keys_of(i0, kv);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = i0 + u * WAVE + lane;
+      const bool in = e < end;
+      const bool gt = in && (exact ? kv[u] >= T : kv[u] > T);
+      const bool eq = in && !exact && kv[u] == T;
+      const uint64_t eqm = ballot(eq);
+      const bool sel = gt || (eq && eq_before + eq_run + mask_rank(eqm) < need);
+      const uint64_t selm = ballot(sel);
+      if (sel) out[sel_before + sel_run + mask_rank(selm)] = src.id(e);
+      eq_run += __popcll(eqm);
+      sel_run += __popcll(selm);
     }
-    const uint64_t eqm = ballot(eq);
-    const bool sel = gt || (eq && eq_before + eq_run + mask_rank(eqm) < need);
-    const uint64_t selm = ballot(sel);
-    if (sel) out[sel_before + sel_run + mask_rank(selm)] = src.id(e);
-    eq_run += __popcll(eqm);
-    sel_run += __popcll(selm);
   }
   __syncthreads();
 }
@@ -255,7 +289,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(
     return;
   }
   if (n <= kRowMax) {
-    for (int i = threadIdx.x; i < n; i += kRowThreads) smem[i] = float_key(row[i]);
+    for_each_key<kRowThreads, 16>(GlobalRow{row}, n, [&](int i, uint32_t key) { smem[i] = key; });
     __syncthreads();
     const LdsKeys src{smem, 0};
     find_threshold<kRowThreads>(src, n, k, hist, st, tmp);
@@ -263,31 +297,45 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(
     return;
   }
   // Long row: threshold from an evenly spaced sample so that ~2k scores survive.
-  for (int i = threadIdx.x; i < kSample; i += kRowThreads) {
-    const int64_t p = (int64_t)i * n / kSample;
-    smem[i] = float_key(row[p]);
+  {
+    constexpr int kPer = kSample / kRowThreads;
+    uint32_t kv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) kv[u] = float_key(row[(int64_t)(threadIdx.x + u * kRowThreads) * n / kSample]);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) smem[threadIdx.x + u * kRowThreads] = kv[u];
   }
   __syncthreads();
   int ks = (int)(((int64_t)2 * k * kSample + n - 1) / n);
   ks = ks < 1 ? 1 : (ks > kSample ? kSample : ks);
   find_threshold<kRowThreads>(LdsKeys{smem, 0}, kSample, ks, hist, st, tmp);
+  // theta = the ks-th largest sample key itself.  (When the radix select stops at a bin
+  // that holds exactly the elements still needed, T is only that bin's lower bound, and
+  // the full row can hold many more scores between T and the sample's ks-th value.)
+  uint32_t mn = 0xFFFFFFFFu;
+  const uint32_t T = st.T;
+  const bool exact = st.exact_ge != 0;
+  for (int i = threadIdx.x; i < kSample; i += kRowThreads) {
+    const uint32_t key = smem[i];
+    if (exact ? key >= T : key == T) mn = min(mn, key);
+  }
+  mn = umin_wave(mn);
+  if ((threadIdx.x & (WAVE - 1)) == 0) tmp[threadIdx.x / WAVE] = (int)mn;
+  __syncthreads();
   if (threadIdx.x == 0) {
-    hdr[r].theta = st.T;
-    hdr[r].done = 0u;
+    uint32_t m = 0xFFFFFFFFu;
+    for (int i = 0; i < kRowThreads / WAVE; ++i) m = min(m, (uint32_t)tmp[i]);
+    hdr[r].theta = m;
   }
 }
 
-// Long rows: compact survivors (key >= theta) per 4096-score chunk, in index order; the
-// last chunk workgroup of a row resolves the exact top-k.
-__global__ __launch_bounds__(kLongThreads) void topk_long_kernel(
+// Long rows, pass 1: compact the survivors (key >= theta) of each 4096-score chunk, in
+// index order, into the chunk's slot of the candidate buffer, and record their count.
+__global__ __launch_bounds__(kLongThreads) void topk_compact_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
-    int32_t* __restrict__ idx, RowHeader* __restrict__ hdr, uint32_t* __restrict__ counts,
-    int max_chunks, uint2* __restrict__ cand) {
-  extern __shared__ uint32_t smem[];  // [kCandCap] keys, [kCandCap] ids, [max_chunks] offsets
-  __shared__ int hist[kHistBins];
-  __shared__ int tmp[64];
-  __shared__ SelState st;
-  __shared__ int is_last;
+    const RowHeader* __restrict__ hdr, uint32_t* __restrict__ counts, int max_chunks,
+    uint2* __restrict__ cand) {
+  __shared__ int wtot[kLongThreads / WAVE];
   constexpr int NW = kLongThreads / WAVE;
   const int r = blockIdx.x;
   const int c = blockIdx.y;
@@ -303,76 +351,105 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(
   const int base = c * kChunk;
   const int end = min(n, base + kChunk);
   constexpr int per = kChunk / NW;
+  constexpr int kIter = per / WAVE;
   const int wb = base + w * per;
-  const int we = min(end, wb + per);
+  // Each lane keeps its keys in registers between the counting and the writing pass.
+  uint32_t key[kIter];
   int cnt = 0;
-  for (int i = wb; i < we; i += WAVE) {
-    const int e = i + lane;
-    const bool keep = e < we && float_key(row[e]) >= theta;
-    cnt += __popcll(ballot(keep));
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int e = wb + it * WAVE + lane;
+    key[it] = float_key(row[min(e, end - 1)]);  // unconditional: all loads in flight at once
   }
-  if (lane == 0) st.wtot[0][w] = cnt;
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int e = wb + it * WAVE + lane;
+    cnt += __popcll(ballot(e < end && key[it] >= theta));
+  }
+  if (lane == 0) wtot[w] = cnt;
   __syncthreads();
   int off = 0;
-  for (int v = 0; v < w; ++v) off += st.wtot[0][v];
+  for (int v = 0; v < w; ++v) off += wtot[v];
   uint2* cr = cand + (int64_t)r * ld + base;
-  for (int i = wb; i < we; i += WAVE) {
-    const int e = i + lane;
-    uint32_t key = 0;
-    bool keep = false;
-    if (e < we) {
-      key = float_key(row[e]);
-      keep = key >= theta;
-    }
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int e = wb + it * WAVE + lane;
+    const bool keep = e < end && key[it] >= theta;
     const uint64_t km = ballot(keep);
-    if (keep) cr[off + mask_rank(km)] = make_uint2(key, (uint32_t)e);
+    if (keep) cr[off + mask_rank(km)] = make_uint2(key[it], (uint32_t)e);
     off += __popcll(km);
   }
   if (threadIdx.x == kLongThreads - 1) counts[(int64_t)r * max_chunks + c] = (uint32_t)off;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = atomicAdd(&hdr[r].done, 1u) == (uint32_t)(nch - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+}
 
-  // ---- resolve (last workgroup of row r)
+// Long rows, pass 2 (one workgroup per row): exact top-k among the survivors in LDS, or
+// among the whole row when the sample threshold kept fewer than k or more than fit.
+__global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
+    int32_t* __restrict__ idx, const uint32_t* __restrict__ counts, int max_chunks,
+    const uint2* __restrict__ cand) {
+  extern __shared__ uint32_t smem[];  // [kCandCap] keys, [kCandCap] ids, [max_chunks] offsets
+  __shared__ int hist[kHistBins];
+  __shared__ int tmp[64];
+  __shared__ SelState st;
+  const int r = blockIdx.x;
+  int64_t n64 = n_valid[r];
+  n64 = n64 < 0 ? 0 : (n64 > ld ? ld : n64);
+  const int n = (int)n64;
+  if (n <= kRowMax || n <= k) return;
+  const int nch = (n + kChunk - 1) / kChunk;
+  const float* row = scores + (int64_t)r * ld;
   uint32_t* keys = smem;
   int* ids = reinterpret_cast<int*>(smem + kCandCap);
   int* offs = reinterpret_cast<int*>(smem + 2 * kCandCap);
   const uint32_t* rc = counts + (int64_t)r * max_chunks;
   int total = 0;  // block-uniform running sum of survivor counts
-  for (int j0 = 0; j0 < nch; j0 += kLongThreads) {
+  for (int j0 = 0; j0 < nch; j0 += kResolveThreads) {
     const int j = j0 + threadIdx.x;
     const int cj = j < nch ? (int)rc[j] : 0;
-    const int ex = block_excl_scan<kLongThreads>(cj, tmp);
+    const int ex = block_excl_scan<kResolveThreads>(cj, tmp);
     if (j < nch) offs[j] = total + ex;
-    if (threadIdx.x == kLongThreads - 1) tmp[63] = ex + cj;
+    if (threadIdx.x == kResolveThreads - 1) tmp[63] = ex + cj;
     __syncthreads();
     total += tmp[63];
     __syncthreads();
   }
   int32_t* out = idx + (int64_t)r * k;
   if (total >= k && total <= kCandCap) {
+    // Flat gather: survivor p lives in chunk j = (the last j with offs[j] <= p); all loads
+    // are independent, so they are in flight together.
     const uint2* rcand = cand + (int64_t)r * ld;
-    for (int j = 0; j < nch; ++j) {
-      const int cj = (j + 1 < nch ? offs[j + 1] : total) - offs[j];
-      for (int i = threadIdx.x; i < cj; i += kLongThreads) {
-        const uint2 p = rcand[(int64_t)j * kChunk + i];
-        keys[offs[j] + i] = p.x;
-        ids[offs[j] + i] = (int)p.y;
+    constexpr int U = 8;
+    for (int p0 = 0; p0 < total; p0 += U * kResolveThreads) {
+      uint2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pc = min(p0 + u * kResolveThreads + (int)threadIdx.x, total - 1);
+        int lo = 0, hi = nch - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (offs[mid] <= pc) lo = mid; else hi = mid - 1;
+        }
+        v[u] = rcand[(int64_t)lo * kChunk + (pc - offs[lo])];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + u * kResolveThreads + (int)threadIdx.x;
+        if (p < total) {
+          keys[p] = v[u].x;
+          ids[p] = (int)v[u].y;
+        }
       }
     }
     __syncthreads();
     const LdsPairs src{keys, ids};
-    find_threshold<kLongThreads>(src, total, k, hist, st, tmp);
-    emit_selected<kLongThreads>(src, total, st, out);
+    find_threshold<kResolveThreads>(src, total, k, hist, st, tmp);
+    emit_selected<kResolveThreads>(src, total, st, out);
   } else {
     const GlobalRow src{row};
-    find_threshold<kLongThreads>(src, n, k, hist, st, tmp);
-    emit_selected<kLongThreads>(src, n, st, out);
+    find_threshold<kResolveThreads>(src, n, k, hist, st, tmp);
+    emit_selected<kResolveThreads>(src, n, st, out);
   }
-  if (threadIdx.x == 0) hdr[r].done = 0u;
 }
 
 struct WsLayout {
@@ -408,10 +485,15 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, 
   topk_rows_kernel<<<R, kRowThreads, row_lds, s>>>(scores, ld, n_valid, k, idx, hdr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.total == 0) return e;
+  uint32_t* counts = reinterpret_cast<uint32_t*>(wsb + L.counts);
+  uint2* cand = reinterpret_cast<uint2*>(wsb + L.cand);
+  topk_compact_kernel<<<dim3(R, L.max_chunks), kLongThreads, 0, s>>>(scores, ld, n_valid, k, hdr, counts,
+                                                                     L.max_chunks, cand);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const size_t long_lds = sizeof(uint32_t) * (2 * (size_t)kCandCap + L.max_chunks);
-  topk_long_kernel<<<dim3(R, L.max_chunks), kLongThreads, long_lds, s>>>(
-      scores, ld, n_valid, k, idx, hdr, reinterpret_cast<uint32_t*>(wsb + L.counts), L.max_chunks,
-      reinterpret_cast<uint2*>(wsb + L.cand));
+  topk_resolve_kernel<<<R, kResolveThreads, long_lds, s>>>(scores, ld, n_valid, k, idx, counts, L.max_chunks,
+                                                        cand);
   return hipGetLastError();
 }
 
