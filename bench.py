@@ -173,6 +173,19 @@ def main():
                "sample": f"{done} sequence-steps of this workload (each a full {int(L.max())}-token "
                          f"index scan, top-k and sparse MLA for one sequence), numpy fp64, {el:.1f} s"}
 
+    # HBM traffic of the indexer from the committed rocprofv3 counter record; null when the
+    # kernel source has changed since the counters were taken.
+    traffic = None
+    try:
+        import hashlib
+        rec = json.load(open(os.path.join(ROOT, "profiles", f"index_fp8_kernel_{cfg['name']}.traffic.json")))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() == rec["source_sha256"]:
+            traffic = {"fetch_bytes": rec["fetch_bytes"], "write_bytes": rec["write_bytes"],
+                       "GB_per_launch": (rec["fetch_bytes"] + rec["write_bytes"]) / 1e9}
+    except (OSError, KeyError, ValueError):
+        traffic = None
+
     out = {
         "metric": METRIC,
         "value": B / (ms_per_step * 1e-3),
@@ -194,7 +207,7 @@ def main():
                    "graph": use_graph, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "index_fp8_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "alg_bytes_per_launch": idx_bytes},
+                     "traffic": traffic, "alg_bytes_per_launch": idx_bytes},
         "step_roofline": {"alg_bytes": step_bytes, "roof_us": roof_us,
                           "frac": roof_us / (ms_per_step * 1e3)},
         "breakdown_us": {"index": idx_us, "topk": float(t_topk.mean()), "sparse_mla": float(t_mla.mean()),
