@@ -41,13 +41,12 @@ struct RowHeader {
   uint32_t pad;
 };
 
+// Block-shared scratch of the selection routines.
 struct SelState {
-  uint32_t T;       // threshold key
-  int need;         // elements equal to T still to take (exact_ge == 0)
-  int exact_ge;     // 1: the selection is exactly { key >= T }
-  uint32_t mn, mx;
-  int digit, above;
-  int wtot[2][16];  // per-wave counts for the emit pass
+  uint32_t wmin[16], wmax[16];  // per-wave key range
+  uint32_t wred[16];            // per-wave partials of a caller's final reduction
+  int wtot[2][16];              // per-wave counts of the emit pass
+  int digit, above, cnt;        // result of a digit search
 };
 
 // ---- element sources --------------------------------------------------------------
@@ -89,129 +88,145 @@ __device__ __forceinline__ void for_each_key(const Src& src, int m, F&& f) {
   }
 }
 
-template <int NT>
-__device__ int block_excl_scan(int x, int* tmp) {
-  constexpr int NW = NT / WAVE;
-  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  int incl = x;
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == WAVE - 1) tmp[w] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int i = 0; i < w; ++i) before += tmp[i];
-  __syncthreads();
-  (void)NW;
-  return before + incl - x;
+// ---- wave primitives: DPP row shifts/rotations and gfx950 lane swaps (no LDS traffic) ----
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
 }
-
-__device__ __forceinline__ uint32_t umin_wave(uint32_t v) {
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp<0x111>(v);        // row_shr:1
+  v += dpp<0x112>(v);        // row_shr:2
+  v += dpp<0x114>(v);        // row_shr:4
+  v += dpp<0x118>(v);        // row_shr:8  -> inclusive within rows of 16
+  v += dpp<0x142, 0xA>(v);   // row_bcast:15 -> rows 1 and 3 add the previous row's total
+  v += dpp<0x143, 0xC>(v);   // row_bcast:31 -> rows 2 and 3 add rows 0-1
   return v;
 }
-__device__ __forceinline__ uint32_t umax_wave(uint32_t v) {
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
+// All-lane reductions: rotations within rows of 16, then swaps across rows and halves.
+template <class F>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, F op) {
+  v = op(v, (uint32_t)dpp<0x128>((int)v));  // row_ror:8
+  v = op(v, (uint32_t)dpp<0x124>((int)v));  // row_ror:4
+  v = op(v, (uint32_t)dpp<0x122>((int)v));  // row_ror:2
+  v = op(v, (uint32_t)dpp<0x121>((int)v));  // row_ror:1
+  const v2i a = __builtin_amdgcn_permlane16_swap((int)v, (int)v, false, false);
+  v = op((uint32_t)a[0], (uint32_t)a[1]);
+  const v2i b = __builtin_amdgcn_permlane32_swap((int)v, (int)v, false, false);
+  return op((uint32_t)b[0], (uint32_t)b[1]);
 }
+struct UMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+struct UMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
 
-// Finds the selection threshold of the top-k (1 <= k <= m) among m elements.  All NT
-// threads of the block must call it.  Result in st (T, need, exact_ge).
+// The top-k threshold: the selection is { key > T } plus the `need` lowest-index elements
+// equal to T, or exactly { key >= T } when `exact`.
+struct Threshold {
+  uint32_t T;
+  int need;
+  bool exact;
+};
+
+// Finds the selection threshold of the top-k (1 <= k <= m) among m elements with
+// range-relative radix digits: the threshold lies in the key interval [lo, hi]; each pass
+// splits it into at most 2048 equal bins of 2^s keys (s chosen from its width), so the
+// histogram resolves wherever the keys actually are, in at most three passes for 32-bit
+// keys.  Histograms alternate between two LDS buffers so clearing the next one needs no
+// extra barrier; one wave scans the bins.  All NT threads must call it.
 template <int NT, class Src>
-__device__ void find_threshold(const Src& src, int m, int k, int* hist, SelState& st, int* tmp) {
+__device__ Threshold find_threshold(const Src& src, int m, int k, int* hist, SelState& st) {
+  constexpr int NW = NT / WAVE;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
   for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
     lmn = min(lmn, key);
     lmx = max(lmx, key);
   });
-  lmn = umin_wave(lmn);
-  lmx = umax_wave(lmx);
+  lmn = wave_reduce(lmn, UMin{});
+  lmx = wave_reduce(lmx, UMax{});
   if (lane == 0) {
-    tmp[w] = (int)lmn;
-    tmp[32 + w] = (int)lmx;
+    st.wmin[w] = lmn;
+    st.wmax[w] = lmx;
   }
+  for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
   __syncthreads();
-  if (tid == 0) {
-    uint32_t a = 0xFFFFFFFFu, b = 0u;
-    for (int i = 0; i < NT / WAVE; ++i) {
-      a = min(a, (uint32_t)tmp[i]);
-      b = max(b, (uint32_t)tmp[32 + i]);
-    }
-    st.mn = a;
-    st.mx = b;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int i = 0; i < NW; ++i) {
+    lo = min(lo, st.wmin[i]);
+    hi = max(hi, st.wmax[i]);
   }
-  __syncthreads();
-  // Range-relative digits: the threshold lies in the key interval [lo, hi]; each pass
-  // splits that interval into at most 2048 equal bins of 2^s keys (s chosen from its
-  // width), so the histogram resolves wherever the keys actually are, in at most three
-  // passes for 32-bit keys.
-  uint32_t lo = st.mn;
-  const uint32_t hi0 = st.mx;
-  uint32_t hi = hi0;
   int need = k;
   bool exact = false;
-  while (hi != lo) {
+  for (int pass = 0; hi != lo; ++pass) {
     const uint32_t width = hi - lo;
     const int s = max(0, 32 - __builtin_clz(width) - 11);
     const int nb = (int)(width >> s) + 1;
-    for (int i = tid; i < nb; i += NT) hist[i] = 0;
-    __syncthreads();
+    int* h = hist + (pass & 1) * kHistBins;
+    int* hn = hist + ((pass + 1) & 1) * kHistBins;
     for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
-      if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> s], 1);
+      if (key >= lo && key <= hi) atomicAdd(&h[(key - lo) >> s], 1);
     });
+    for (int i = tid; i < kHistBins; i += NT) hn[i] = 0;
     __syncthreads();
-    // Thread t owns the t-th group of bins counted from the top.
-    constexpr int kPer = (kHistBins + NT - 1) / NT;
-    const int lo_bin = nb - (tid + 1) * kPer;
-    int local = 0;
-    for (int j = 0; j < kPer; ++j) {
-      const int b = lo_bin + j;
-      if (b >= 0 && b < nb) local += hist[b];
-    }
-    int run = block_excl_scan<NT>(local, tmp);  // elements in bins above my group
-    for (int j = kPer - 1; j >= 0; --j) {
-      const int b = lo_bin + j;
-      if (b < 0 || b >= nb) continue;
-      const int c = hist[b];
-      if (run < need && run + c >= need) {
-        st.digit = b;
-        st.above = run;
+    if (w == 0) {
+      // Lane l owns bins [nb - 32(l+1), nb - 32l), counted from the top; its 32 counts stay
+      // in registers so the crossing search needs no further LDS reads.
+      constexpr int kPer = kHistBins / WAVE;
+      const int top = nb - kPer * lane;
+      int cb[kPer];
+      int local = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int b = top - 1 - j;
+        cb[j] = b >= 0 ? h[max(b, 0)] : 0;
+        local += cb[j];
       }
-      run += c;
+      const int incl = wave_incl_scan(local);
+      int run = incl - local;
+      if (run < need && incl >= need) {
+        int dj = 0, above = run, cnt = 0;
+        bool found = false;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          if (!found && run + cb[j] >= need) {
+            found = true;
+            dj = j;
+            above = run;
+            cnt = cb[j];
+          }
+          run += cb[j];
+        }
+        st.digit = top - 1 - dj;
+        st.above = above;
+        st.cnt = cnt;
+      }
     }
     __syncthreads();
     const int d = st.digit;
     need -= st.above;
-    const int cnt = hist[d];
+    const int cnt = st.cnt;
     const uint32_t new_lo = lo + ((uint32_t)d << s);
     const uint64_t top = (uint64_t)new_lo + ((uint64_t)1 << s) - 1;
     hi = top < (uint64_t)hi ? (uint32_t)top : hi;
     lo = new_lo;
-    __syncthreads();
     if (cnt == need) {  // every key of the bin is taken: the selection is { key >= lo }
       exact = true;
       break;
     }
   }
-  const uint32_t prefix = lo;
-  if (tid == 0) {
-    st.T = prefix;
-    st.need = need;
-    st.exact_ge = exact ? 1 : 0;
-  }
-  __syncthreads();
+  return Threshold{lo, need, exact};
 }
 
 // Writes the ids of the selected elements, in ascending position order, to out[0..k).
+// Each wave walks a contiguous position range with ballots, so elements equal to T are
+// taken lowest position first.
 template <int NT, class Src>
-__device__ void emit_selected(const Src& src, int m, SelState& st, int32_t* __restrict__ out) {
+__device__ void emit_selected(const Src& src, int m, const Threshold& th, SelState& st,
+                              int32_t* __restrict__ out) {
   constexpr int NW = NT / WAVE;
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  const uint32_t T = st.T;
-  const bool exact = st.exact_ge != 0;
-  const int need = st.need;
+  const uint32_t T = th.T;
+  const bool exact = th.exact;
+  const int need = th.need;
   const int per = ((m + NW - 1) / NW + WAVE - 1) / WAVE * WAVE;
   const int beg = w * per;
   const int end = min(m, beg + per);
@@ -266,7 +281,6 @@ __device__ void emit_selected(const Src& src, int m, SelState& st, int32_t* __re
       sel_run += __popcll(selm);
     }
   }
-  __syncthreads();
 }
 
 // One workgroup per row: trivial rows, LDS-resident rows, or the sample threshold of
@@ -275,8 +289,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
     int32_t* __restrict__ idx, RowHeader* __restrict__ hdr) {
   extern __shared__ uint32_t smem[];
-  __shared__ int hist[kHistBins];
-  __shared__ int tmp[64];
+  __shared__ int hist[2 * kHistBins];
   __shared__ SelState st;
   const int r = blockIdx.x;
   int64_t n64 = n_valid[r];
@@ -292,8 +305,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(
     for_each_key<kRowThreads, 16>(GlobalRow{row}, n, [&](int i, uint32_t key) { smem[i] = key; });
     __syncthreads();
     const LdsKeys src{smem, 0};
-    find_threshold<kRowThreads>(src, n, k, hist, st, tmp);
-    emit_selected<kRowThreads>(src, n, st, out);
+    const Threshold th = find_threshold<kRowThreads>(src, n, k, hist, st);
+    emit_selected<kRowThreads>(src, n, th, st, out);
     return;
   }
   // Long row: threshold from an evenly spaced sample so that ~2k scores survive.
@@ -308,23 +321,22 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(
   __syncthreads();
   int ks = (int)(((int64_t)2 * k * kSample + n - 1) / n);
   ks = ks < 1 ? 1 : (ks > kSample ? kSample : ks);
-  find_threshold<kRowThreads>(LdsKeys{smem, 0}, kSample, ks, hist, st, tmp);
-  // theta = the ks-th largest sample key itself.  (When the radix select stops at a bin
-  // that holds exactly the elements still needed, T is only that bin's lower bound, and
-  // the full row can hold many more scores between T and the sample's ks-th value.)
+  const Threshold th = find_threshold<kRowThreads>(LdsKeys{smem, 0}, kSample, ks, hist, st);
+  // theta = the ks-th largest sample key itself.  (When the search stops at a bin that holds
+  // exactly the elements still needed, T is only that bin's lower bound, and the full row
+  // can hold many more scores between T and the sample's ks-th value.)
   uint32_t mn = 0xFFFFFFFFu;
-  const uint32_t T = st.T;
-  const bool exact = st.exact_ge != 0;
   for (int i = threadIdx.x; i < kSample; i += kRowThreads) {
     const uint32_t key = smem[i];
-    if (exact ? key >= T : key == T) mn = min(mn, key);
+    if (th.exact ? key >= th.T : key == th.T) mn = min(mn, key);
   }
-  mn = umin_wave(mn);
-  if ((threadIdx.x & (WAVE - 1)) == 0) tmp[threadIdx.x / WAVE] = (int)mn;
+  mn = wave_reduce(mn, UMin{});
+  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  if (lane == 0) st.wred[w] = mn;  // not wmin: slower waves may still read that
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t m = 0xFFFFFFFFu;
-    for (int i = 0; i < kRowThreads / WAVE; ++i) m = min(m, (uint32_t)tmp[i]);
+    for (int i = 0; i < kRowThreads / WAVE; ++i) m = min(m, st.wred[i]);
     hdr[r].theta = m;
   }
 }
@@ -388,10 +400,10 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
     int32_t* __restrict__ idx, const uint32_t* __restrict__ counts, int max_chunks,
     const uint2* __restrict__ cand) {
-  extern __shared__ uint32_t smem[];  // [kCandCap] keys, [kCandCap] ids, [max_chunks] offsets
-  __shared__ int hist[kHistBins];
-  __shared__ int tmp[64];
+  extern __shared__ uint32_t smem[];  // [kCandCap] keys, [kCandCap] ids, [max_chunks + 1] offsets
+  __shared__ int hist[2 * kHistBins];
   __shared__ SelState st;
+  constexpr int NW = kResolveThreads / WAVE;
   const int r = blockIdx.x;
   int64_t n64 = n_valid[r];
   n64 = n64 < 0 ? 0 : (n64 > ld ? ld : n64);
@@ -403,52 +415,50 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
   int* ids = reinterpret_cast<int*>(smem + kCandCap);
   int* offs = reinterpret_cast<int*>(smem + 2 * kCandCap);
   const uint32_t* rc = counts + (int64_t)r * max_chunks;
-  int total = 0;  // block-uniform running sum of survivor counts
-  for (int j0 = 0; j0 < nch; j0 += kResolveThreads) {
-    const int j = j0 + threadIdx.x;
-    const int cj = j < nch ? (int)rc[j] : 0;
-    const int ex = block_excl_scan<kResolveThreads>(cj, tmp);
-    if (j < nch) offs[j] = total + ex;
-    if (threadIdx.x == kResolveThreads - 1) tmp[63] = ex + cj;
-    __syncthreads();
-    total += tmp[63];
-    __syncthreads();
+  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  if (w == 0) {  // exclusive prefix of the survivor counts, 64 chunks per step
+    int carry = 0;
+    for (int j0 = 0; j0 < nch; j0 += WAVE) {
+      const int j = j0 + lane;
+      const int cj = j < nch ? (int)rc[j] : 0;
+      const int incl = wave_incl_scan(cj);
+      if (j < nch) offs[j] = carry + incl - cj;
+      carry += __shfl(incl, WAVE - 1);
+    }
+    if (lane == 0) offs[nch] = carry;
   }
+  __syncthreads();
+  const int total = offs[nch];
   int32_t* out = idx + (int64_t)r * k;
   if (total >= k && total <= kCandCap) {
-    // Flat gather: survivor p lives in chunk j = (the last j with offs[j] <= p); all loads
-    // are independent, so they are in flight together.
+    // Wave w copies chunks w, w + NW, ...; each lane issues up to U loads per chunk group
+    // before storing, so typical chunks (~2k/32 survivors) cost one round trip.
     const uint2* rcand = cand + (int64_t)r * ld;
-    constexpr int U = 8;
-    for (int p0 = 0; p0 < total; p0 += U * kResolveThreads) {
-      uint2 v[U];
+    constexpr int U = 4;
+    for (int j = w; j < nch; j += NW) {
+      const int o = offs[j], cj = offs[j + 1] - o;
+      for (int i0 = 0; i0 < cj; i0 += U * WAVE) {
+        uint2 v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int pc = min(p0 + u * kResolveThreads + (int)threadIdx.x, total - 1);
-        int lo = 0, hi = nch - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (offs[mid] <= pc) lo = mid; else hi = mid - 1;
-        }
-        v[u] = rcand[(int64_t)lo * kChunk + (pc - offs[lo])];
-      }
+        for (int u = 0; u < U; ++u) v[u] = rcand[(int64_t)j * kChunk + min(i0 + u * WAVE + lane, cj - 1)];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int p = p0 + u * kResolveThreads + (int)threadIdx.x;
-        if (p < total) {
-          keys[p] = v[u].x;
-          ids[p] = (int)v[u].y;
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * WAVE + lane;
+          if (i < cj) {
+            keys[o + i] = v[u].x;
+            ids[o + i] = (int)v[u].y;
+          }
         }
       }
     }
     __syncthreads();
     const LdsPairs src{keys, ids};
-    find_threshold<kResolveThreads>(src, total, k, hist, st, tmp);
-    emit_selected<kResolveThreads>(src, total, st, out);
+    const Threshold th = find_threshold<kResolveThreads>(src, total, k, hist, st);
+    emit_selected<kResolveThreads>(src, total, th, st, out);
   } else {
     const GlobalRow src{row};
-    find_threshold<kResolveThreads>(src, n, k, hist, st, tmp);
-    emit_selected<kResolveThreads>(src, n, st, out);
+    const Threshold th = find_threshold<kResolveThreads>(src, n, k, hist, st);
+    emit_selected<kResolveThreads>(src, n, th, st, out);
   }
 }
 
@@ -491,7 +501,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, 
                                                                      L.max_chunks, cand);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t long_lds = sizeof(uint32_t) * (2 * (size_t)kCandCap + L.max_chunks);
+  const size_t long_lds = sizeof(uint32_t) * (2 * (size_t)kCandCap + L.max_chunks + 1);
   topk_resolve_kernel<<<R, kResolveThreads, long_lds, s>>>(scores, ld, n_valid, k, idx, counts, L.max_chunks,
                                                         cand);
   return hipGetLastError();
