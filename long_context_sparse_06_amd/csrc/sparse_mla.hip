@@ -267,46 +267,53 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   }
 }
 
-// Log-sum-exp merge of the split partials: one 64-thread group per (row, head),
-// 8 value columns per thread.
+// Log-sum-exp merge of the split partials: 128 threads per (row, head), 4 value columns
+// per thread.  Splits are taken 16 at a time with every load of a batch (values and the
+// (max, sum) pairs alike) issued before any is used, so a typical merge is one round trip;
+// batches after the first rescale the running sums to the new maximum.
+constexpr int kCombineBatch = 16;
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int RH, int H, int n_split,
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
-  const int pair = blockIdx.x * 4 + threadIdx.x / WAVE;
+  const int pair = blockIdx.x * 2 + threadIdx.x / 128;
   if (pair >= RH) return;
   const int r = pair / H, h = pair % H;
-  const int lane = threadIdx.x & (WAVE - 1);
+  const int t = threadIdx.x & 127;
   const int64_t p0 = (int64_t)r * n_split * H + h;  // partial of split s at p0 + s * H
-  // Pass 1 reads only the (max, sum) pairs; pass 2 issues every split's value loads at
-  // once with its weight computed up front (no load depends on another).
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < n_split; ++s) {
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * (p0 + (int64_t)s * H));
-    M = ml.y > 0.0f ? fmaxf(M, ml.x) : M;
-  }
-  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float L = 0.0f;
-#pragma unroll 8
-  for (int s = 0; s < n_split; ++s) {
-    const int64_t pr = p0 + (int64_t)s * H;
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
-    const float f = (ml.y > 0.0f && M != -INFINITY) ? exp2f(ml.x - M) : 0.0f;
-    L += ml.y > 0.0f ? ml.y * f : 0.0f;
-    const float4* po = reinterpret_cast<const float4*>(part_o + pr * kDv + 8 * lane);
-    const float4 a = po[0], b = po[1];
-    o[0] += a.x * f; o[1] += a.y * f; o[2] += a.z * f; o[3] += a.w * f;
-    o[4] += b.x * f; o[5] += b.y * f; o[6] += b.z * f; o[7] += b.w * f;
+  float M = -INFINITY, L = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
+    float2 ml[kCombineBatch];
+    float4 v[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int64_t pr = p0 + (int64_t)min(s0 + u, n_split - 1) * H;
+      ml[u] = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
+      v[u] = *reinterpret_cast<const float4*>(part_o + pr * kDv + 4 * t);
+    }
+    float Mb = M;
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)
+      if (s0 + u < n_split && ml[u].y > 0.0f) Mb = fmaxf(Mb, ml[u].x);
+    const float c = M == -INFINITY ? 0.0f : exp2f(M - Mb);
+    L *= c;
+    acc.x *= c; acc.y *= c; acc.z *= c; acc.w *= c;
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const bool valid = s0 + u < n_split && ml[u].y > 0.0f;
+      const float f = valid ? exp2f(ml[u].x - Mb) : 0.0f;
+      L += valid ? ml[u].y * f : 0.0f;
+      acc.x += v[u].x * f; acc.y += v[u].y * f; acc.z += v[u].z * f; acc.w += v[u].w * f;
+    }
+    M = Mb;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  uint32_t pk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    pk[i] = f32_to_bf16(o[2 * i] * inv) | ((uint32_t)f32_to_bf16(o[2 * i + 1] * inv) << 16);
-  *reinterpret_cast<uint4*>(out + ((int64_t)r * H + h) * kDv + 8 * lane) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-  if (lse && lane == 0) lse[(int64_t)r * H + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  const uint32_t lo = f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+  const uint32_t hi = f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+  *reinterpret_cast<uint2*>(out + ((int64_t)r * H + h) * kDv + 4 * t) = make_uint2(lo, hi);
+  if (lse && t == 0) lse[(int64_t)r * H + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // Any shape, fp32 or bf16: one workgroup per (row, head), logits staged in LDS.
@@ -427,7 +434,7 @@ hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split <= 1) return e;
   const int RH = R * H;
-  mla_combine_kernel<<<(RH + 3) / 4, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
+  mla_combine_kernel<<<(RH + 1) / 2, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
   return hipGetLastError();
 }
 

@@ -9,18 +9,23 @@
 // Method: radix select on order-preserving 32-bit keys held in LDS.  A min/max pass
 // first strips the bits all keys share, so the 11-bit histogram digits land where the
 // keys actually differ; each digit pass narrows to one bin until either that bin holds
-// exactly the elements still needed or the full key (the threshold T) is known.  The
-// emit pass walks each wave's contiguous index range with ballots, so the elements equal
-// to T are taken lowest index first and the output comes out sorted.
+// exactly the elements still needed or the full key (the threshold T) is known.  Every
+// search step is block-parallel (DPP wave scans, per-wave totals through LDS); no phase
+// runs on a single wave.  The emit pass walks each wave's contiguous index range with
+// ballots, so the elements equal to T are taken lowest index first and the output comes
+// out sorted.
 //
 // Rows up to kRowMax scores are selected by one workgroup entirely in LDS.  Longer rows
 // (decode at 128k context) take three launches: one workgroup per row draws an evenly
 // spaced sample and sets a threshold theta whose expected survivor count is ~2k; many
 // workgroups per row compact the survivors (in index order); one workgroup per row then
-// resolves the exact top-k among them in LDS.  The hand-offs are kernel boundaries: an
-// in-kernel device-scope fence costs a whole-L2 writeback and invalidate on this chip.
+// gathers them into LDS, histogramming them into 4096 bins above theta on the way, so the
+// bin holding the k-th largest survivor is known after one block scan, and ranks the few
+// keys of that bin by direct comparison.  The hand-offs are kernel boundaries: an in-kernel
+// device-scope fence costs a whole-L2 writeback and invalidate on this chip.
 // Correctness never depends on the sample: if fewer than k or more than fit in LDS
-// survive, the resolve selects from the full row in global memory instead.
+// survive, the resolve selects from the full row in global memory instead, and a
+// crowded boundary bin falls back to the radix select over the survivors.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,21 +37,28 @@ constexpr int kSample = 2048;      // sample size for longer rows
 constexpr int kChunk = 4096;       // scores per workgroup in the long-row compaction pass
 constexpr int kCandCap = 12288;    // survivors resolvable in LDS (96 KiB of key/index pairs)
 constexpr int kHistBins = 2048;    // 11-bit digits
+constexpr int kPassMax = 3;        // range-relative 11-bit digits resolve 32-bit keys in 3 passes
+constexpr int kSurvBins = 4096;    // survivor histogram of a long row
+constexpr int kTieMax = 256;       // largest boundary bin ranked by pairwise comparison
 constexpr int kRowThreads = 1024;
-constexpr int kLongThreads = 256;    // compaction workgroups
+constexpr int kLongThreads = 256;  // compaction workgroups
 constexpr int kResolveThreads = 1024;
 
 struct RowHeader {
   uint32_t theta;  // sample threshold key of a long row
-  uint32_t pad;
+  uint32_t shift;  // survivor bin of key = min((key - theta) >> shift, kSurvBins - 1)
 };
 
 // Block-shared scratch of the selection routines.
 struct SelState {
-  uint32_t wmin[16], wmax[16];  // per-wave key range
-  uint32_t wred[16];            // per-wave partials of a caller's final reduction
-  int wtot[2][16];              // per-wave counts of the emit pass
-  int digit, above, cnt;        // result of a digit search
+  uint32_t wmin[16], wmax[16];      // per-wave key range
+  uint32_t wred[16];                // per-wave partials of a caller's final reduction
+  alignas(16) int wscan[16];        // per-wave bin totals of a crossing search
+  alignas(16) int wtot[2][16];      // per-wave counts of the emit pass
+  int digit, above, cnt;            // result of a crossing search
+  uint32_t tie_T;                   // result of the boundary-bin ranking
+  int tie_need;
+  int ntie;
 };
 
 // ---- element sources --------------------------------------------------------------
@@ -118,136 +130,182 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t v, F op) {
 struct UMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
 struct UMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
 
+__device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
 // The top-k threshold: the selection is { key > T } plus the `need` lowest-index elements
-// equal to T, or exactly { key >= T } when `exact`.
+// equal to T, or exactly { key >= T } when `exact`.  `top` is the largest key seen.
 struct Threshold {
   uint32_t T;
   int need;
   bool exact;
+  uint32_t top;
 };
 
-// Finds the selection threshold of the top-k (1 <= k <= m) among m elements with
-// range-relative radix digits: the threshold lies in the key interval [lo, hi]; each pass
-// splits it into at most 2048 equal bins of 2^s keys (s chosen from its width), so the
-// histogram resolves wherever the keys actually are, in at most three passes for 32-bit
-// keys.  Histograms alternate between two LDS buffers so clearing the next one needs no
-// extra barrier; one wave scans the bins.  All NT threads must call it.
-template <int NT, class Src>
-__device__ Threshold find_threshold(const Src& src, int m, int k, int* hist, SelState& st) {
-  constexpr int NW = NT / WAVE;
+// Given one thread's PER bin counts cb[0..PER) (its bins in descending order, the first
+// being bin `first`), finds the bin where the count from the top reaches `need` within the
+// wave whose bins these are; `before` counts everything above the wave.  Returns the
+// crossing (bin, count above it, its count), the same in every lane.  The caller
+// guarantees the crossing lies in this wave.
+template <int PER>
+__device__ __forceinline__ void wave_crossing(const int (&cb)[PER], int first, int before, int need,
+                                              int& digit, int& above, int& cnt) {
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) local += cb[j];
+  const int incl = wave_incl_scan(local);
+  int run = before + incl - local;
+  const bool mine = run < need && run + local >= need;
+  int dj = 0, ab = 0, cn = 0;
+  bool found = false;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool hit = !found && run + cb[j] >= need;
+    dj = hit ? j : dj;
+    ab = hit ? run : ab;
+    cn = hit ? cb[j] : cn;
+    found = found || hit;
+    run += cb[j];
+  }
+  const int cl = (int)__builtin_ctzll(ballot(mine));
+  digit = readlane(first - dj, cl);
+  above = readlane(ab, cl);
+  cnt = readlane(cn, cl);
+}
+
+// Publishes the block's key range for find_threshold (each thread passes the min and max of
+// its own keys) and clears the histogram buffers; the caller's next barrier publishes both.
+template <int NT>
+__device__ __forceinline__ void publish_range(uint32_t lmn, uint32_t lmx, int* hist, SelState& st) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
-  for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
-    lmn = min(lmn, key);
-    lmx = max(lmx, key);
-  });
   lmn = wave_reduce(lmn, UMin{});
   lmx = wave_reduce(lmx, UMax{});
   if (lane == 0) {
     st.wmin[w] = lmn;
     st.wmax[w] = lmx;
   }
-  for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
-  __syncthreads();
+  for (int i = tid; i < kPassMax * kHistBins / 4; i += NT) reinterpret_cast<int4*>(hist)[i] = make_int4(0, 0, 0, 0);
+}
+
+// Finds the selection threshold of the top-k (1 <= k <= m) among m elements with
+// range-relative radix digits: the threshold lies in the key interval [lo, hi]; each pass
+// splits it into at most 2048 equal bins of 2^s keys (s chosen from its width), so the
+// histogram resolves wherever the keys actually are, in at most three passes.  Each pass
+// has two barriers: after the histogram, and after the per-wave totals; every wave then
+// finds the crossing wave from the totals and rescans that wave's bins itself, so the
+// result needs no broadcast.  Each pass has its own histogram buffer (cleared up front),
+// so no clearing races a slower wave's rescan.  All NT threads must call it.
+//
+// RANGED: the caller has already run publish_range (and a barrier) with every thread's key
+// range, typically while it loaded the keys, which saves a pass and a barrier.  `slack`
+// lets the search stop early, with `exact` set, once the bin holds at most `slack` more
+// elements than needed -- only for callers content with up to k + slack elements >= T.
+template <int NT, bool RANGED = false, class Src>
+__device__ Threshold find_threshold(const Src& src, int m, int k, int* hist, SelState& st,
+                                    int slack = 0) {
+  constexpr int NW = NT / WAVE;
+  constexpr int PER = kHistBins / NT;
+  static_assert(PER * NT == kHistBins, "bins per thread");
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  if (!RANGED) {
+    uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
+    for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
+      lmn = min(lmn, key);
+      lmx = max(lmx, key);
+    });
+    publish_range<NT>(lmn, lmx, hist, st);
+    __syncthreads();
+  }
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
   for (int i = 0; i < NW; ++i) {
     lo = min(lo, st.wmin[i]);
     hi = max(hi, st.wmax[i]);
   }
+  const uint32_t top = hi;
   int need = k;
   bool exact = false;
-  for (int pass = 0; hi != lo; ++pass) {
+  for (int pass = 0; pass < kPassMax && hi != lo; ++pass) {
     const uint32_t width = hi - lo;
     const int s = max(0, 32 - __builtin_clz(width) - 11);
     const int nb = (int)(width >> s) + 1;
-    int* h = hist + (pass & 1) * kHistBins;
-    int* hn = hist + ((pass + 1) & 1) * kHistBins;
+    int* h = hist + pass * kHistBins;
     for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
       if (key >= lo && key <= hi) atomicAdd(&h[(key - lo) >> s], 1);
     });
-    for (int i = tid; i < kHistBins; i += NT) hn[i] = 0;
     __syncthreads();
-    if (w == 0) {
-      // Lane l owns bins [nb - 32(l+1), nb - 32l), counted from the top; its 32 counts stay
-      // in registers so the crossing search needs no further LDS reads.
-      constexpr int kPer = kHistBins / WAVE;
-      const int top = nb - kPer * lane;
-      int cb[kPer];
-      int local = 0;
+    // Thread t owns bins nb-1-PER*t-j (j < PER): bins counted from the top.
+    int cb[PER];
+    int local = 0;
+    const int first = nb - 1 - PER * tid;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int b = top - 1 - j;
-        cb[j] = b >= 0 ? h[max(b, 0)] : 0;
-        local += cb[j];
-      }
-      const int incl = wave_incl_scan(local);
-      int run = incl - local;
-      if (run < need && incl >= need) {
-        int dj = 0, above = run, cnt = 0;
-        bool found = false;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          if (!found && run + cb[j] >= need) {
-            found = true;
-            dj = j;
-            above = run;
-            cnt = cb[j];
-          }
-          run += cb[j];
-        }
-        st.digit = top - 1 - dj;
-        st.above = above;
-        st.cnt = cnt;
-      }
+    for (int j = 0; j < PER; ++j) {
+      const int b = first - j;
+      const int v = h[max(b, 0)];
+      cb[j] = b >= 0 ? v : 0;
+      local += cb[j];
     }
+    const int incl = wave_incl_scan(local);
+    if (lane == WAVE - 1) st.wscan[w] = incl;
     __syncthreads();
-    const int d = st.digit;
-    need -= st.above;
-    const int cnt = st.cnt;
+    int before = 0, vc = -1;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const int tv = st.wscan[v];
+      const bool hit = vc < 0 && before + tv >= need;
+      before += (vc < 0 && !hit) ? tv : 0;
+      vc = hit ? v : vc;
+    }
+    // Rescan the crossing wave's bins (the same PER per lane that wave read).
+    const int first2 = nb - 1 - PER * (vc * WAVE + lane);
+    int cb2[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int b = first2 - j;
+      const int v = h[max(b, 0)];
+      cb2[j] = b >= 0 ? v : 0;
+    }
+    int d, above, cnt;
+    wave_crossing<PER>(cb2, first2, before, need, d, above, cnt);
+    need -= above;
     const uint32_t new_lo = lo + ((uint32_t)d << s);
-    const uint64_t top = (uint64_t)new_lo + ((uint64_t)1 << s) - 1;
-    hi = top < (uint64_t)hi ? (uint32_t)top : hi;
+    const uint64_t top_of_bin = (uint64_t)new_lo + ((uint64_t)1 << s) - 1;
+    hi = top_of_bin < (uint64_t)hi ? (uint32_t)top_of_bin : hi;
     lo = new_lo;
-    if (cnt == need) {  // every key of the bin is taken: the selection is { key >= lo }
+    if (cnt - need <= slack) {  // every key of the bin is taken: the selection is { key >= lo }
       exact = true;
       break;
     }
   }
-  return Threshold{lo, need, exact};
+  return Threshold{lo, need, exact, top};
 }
 
 // Writes the ids of the selected elements, in ascending position order, to out[0..k).
 // Each wave walks a contiguous position range with ballots, so elements equal to T are
-// taken lowest position first.
+// taken lowest position first; the waves' output offsets come from two DPP scans over
+// the per-wave counts.  Predicates combine with bitwise operators so the element loop is
+// straight-line mask arithmetic, and ids are read together with keys, before any is used.
 template <int NT, class Src>
 __device__ void emit_selected(const Src& src, int m, const Threshold& th, SelState& st,
                               int32_t* __restrict__ out) {
   constexpr int NW = NT / WAVE;
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
   const uint32_t T = th.T;
-  const bool exact = th.exact;
-  const int need = th.need;
+  const bool ex = th.exact;
+  const int need = ex ? 0 : th.need;
   const int per = ((m + NW - 1) / NW + WAVE - 1) / WAVE * WAVE;
   const int beg = w * per;
   const int end = min(m, beg + per);
   constexpr int U = 8;  // rounds of 64 whose keys are read before they are used
-  auto keys_of = [&](int i0, uint32_t (&kv)[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = i0 + u * WAVE + lane;
-      kv[u] = src.key(min(e, end - 1));
-    }
-  };
   int cgt = 0, ceq = 0;
   for (int i0 = beg; i0 < end; i0 += U * WAVE) {
     uint32_t kv[U];
-    keys_of(i0, kv);
+#pragma unroll
+    for (int u = 0; u < U; ++u) kv[u] = src.key(min(i0 + u * WAVE + lane, end - 1));
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = i0 + u * WAVE + lane;
-      const bool in = e < end;
-      cgt += __popcll(ballot(in && (exact ? kv[u] >= T : kv[u] > T)));
-      ceq += __popcll(ballot(in && !exact && kv[u] == T));
+      const bool in = i0 + u * WAVE + lane < end;
+      cgt += __popcll(ballot(in & ((kv[u] > T) | (ex & (kv[u] == T)))));
+      ceq += __popcll(ballot(in & !ex & (kv[u] == T)));
     }
   }
   if (lane == 0) {
@@ -255,99 +313,53 @@ __device__ void emit_selected(const Src& src, int m, const Threshold& th, SelSta
     st.wtot[1][w] = ceq;
   }
   __syncthreads();
-  int eq_before = 0, sel_before = 0;
-  for (int v = 0; v < w; ++v) {
-    const int e_v = st.wtot[1][v];
-    int take = need - eq_before;
-    take = take < 0 ? 0 : (take > e_v ? e_v : take);
-    sel_before += st.wtot[0][v] + take;
-    eq_before += e_v;
-  }
+  // Lane v < NW stands for wave v: ties are taken in wave order until `need` is met.
+  const int gt_v = lane < NW ? st.wtot[0][lane] : 0;
+  const int eq_v = lane < NW ? st.wtot[1][lane] : 0;
+  const int eq_before_v = wave_incl_scan(eq_v) - eq_v;
+  const int take_v = min(max(need - eq_before_v, 0), eq_v);
+  const int sel_v = gt_v + take_v;
+  const int sel_before_v = wave_incl_scan(sel_v) - sel_v;
+  const int eq_before = readlane(eq_before_v, w);
+  const int sel_before = readlane(sel_before_v, w);
   int eq_run = 0, sel_run = 0;
   for (int i0 = beg; i0 < end; i0 += U * WAVE) {
     uint32_t kv[U];
-    keys_of(i0, kv);
+    int iv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = i0 + u * WAVE + lane;
-      const bool in = e < end;
-      const bool gt = in && (exact ? kv[u] >= T : kv[u] > T);
-      const bool eq = in && !exact && kv[u] == T;
+      const int e = min(i0 + u * WAVE + lane, end - 1);
+      kv[u] = src.key(e);
+      iv[u] = src.id(e);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = i0 + u * WAVE + lane < end;
+      const bool gt = in & ((kv[u] > T) | (ex & (kv[u] == T)));
+      const bool eq = in & !ex & (kv[u] == T);
       const uint64_t eqm = ballot(eq);
-      const bool sel = gt || (eq && eq_before + eq_run + mask_rank(eqm) < need);
+      const bool sel = gt | (eq & (eq_before + eq_run + mask_rank(eqm) < need));
       const uint64_t selm = ballot(sel);
-      if (sel) out[sel_before + sel_run + mask_rank(selm)] = src.id(e);
+      if (sel) out[sel_before + sel_run + mask_rank(selm)] = iv[u];
       eq_run += __popcll(eqm);
       sel_run += __popcll(selm);
     }
   }
 }
 
-// One workgroup per row: trivial rows, LDS-resident rows, or the sample threshold of
-// long rows.
-__global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(
+// Long rows, pass 1 (R x chunks workgroups): every workgroup of a row derives the same
+// sample threshold theta -- the ks-th largest of kSample evenly spaced scores, ks chosen
+// so that ~2k scores of the row are expected to reach it -- while the loads of its own
+// 4096-score chunk are in flight, then compacts the chunk's survivors (key >= theta) in
+// index order into the chunk's slot of the candidate buffer and records their count.
+// Chunk 0 also records theta and the survivor-bin shift for the resolve.
+__global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
-    int32_t* __restrict__ idx, RowHeader* __restrict__ hdr) {
-  extern __shared__ uint32_t smem[];
-  __shared__ int hist[2 * kHistBins];
-  __shared__ SelState st;
-  const int r = blockIdx.x;
-  int64_t n64 = n_valid[r];
-  n64 = n64 < 0 ? 0 : (n64 > ld ? ld : n64);
-  const int n = (int)n64;
-  int32_t* out = idx + (int64_t)r * k;
-  const float* row = scores + (int64_t)r * ld;
-  if (n <= k) {
-    for (int i = threadIdx.x; i < k; i += kRowThreads) out[i] = i < n ? i : -1;
-    return;
-  }
-  if (n <= kRowMax) {
-    for_each_key<kRowThreads, 16>(GlobalRow{row}, n, [&](int i, uint32_t key) { smem[i] = key; });
-    __syncthreads();
-    const LdsKeys src{smem, 0};
-    const Threshold th = find_threshold<kRowThreads>(src, n, k, hist, st);
-    emit_selected<kRowThreads>(src, n, th, st, out);
-    return;
-  }
-  // Long row: threshold from an evenly spaced sample so that ~2k scores survive.
-  {
-    constexpr int kPer = kSample / kRowThreads;
-    uint32_t kv[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) kv[u] = float_key(row[(int64_t)(threadIdx.x + u * kRowThreads) * n / kSample]);
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) smem[threadIdx.x + u * kRowThreads] = kv[u];
-  }
-  __syncthreads();
-  int ks = (int)(((int64_t)2 * k * kSample + n - 1) / n);
-  ks = ks < 1 ? 1 : (ks > kSample ? kSample : ks);
-  const Threshold th = find_threshold<kRowThreads>(LdsKeys{smem, 0}, kSample, ks, hist, st);
-  // theta = the ks-th largest sample key itself.  (When the search stops at a bin that holds
-  // exactly the elements still needed, T is only that bin's lower bound, and the full row
-  // can hold many more scores between T and the sample's ks-th value.)
-  uint32_t mn = 0xFFFFFFFFu;
-  for (int i = threadIdx.x; i < kSample; i += kRowThreads) {
-    const uint32_t key = smem[i];
-    if (th.exact ? key >= th.T : key == th.T) mn = min(mn, key);
-  }
-  mn = wave_reduce(mn, UMin{});
-  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  if (lane == 0) st.wred[w] = mn;  // not wmin: slower waves may still read that
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t m = 0xFFFFFFFFu;
-    for (int i = 0; i < kRowThreads / WAVE; ++i) m = min(m, st.wred[i]);
-    hdr[r].theta = m;
-  }
-}
-
-// Long rows, pass 1: compact the survivors (key >= theta) of each 4096-score chunk, in
-// index order, into the chunk's slot of the candidate buffer, and record their count.
-__global__ __launch_bounds__(kLongThreads) void topk_compact_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
-    const RowHeader* __restrict__ hdr, uint32_t* __restrict__ counts, int max_chunks,
+    RowHeader* __restrict__ hdr, uint32_t* __restrict__ counts, int max_chunks,
     uint2* __restrict__ cand) {
-  __shared__ int wtot[kLongThreads / WAVE];
+  __shared__ uint32_t samp[kSample];
+  __shared__ __attribute__((aligned(16))) int hist[kPassMax * kHistBins];
+  __shared__ SelState st;
   constexpr int NW = kLongThreads / WAVE;
   const int r = blockIdx.x;
   const int c = blockIdx.y;
@@ -358,30 +370,73 @@ __global__ __launch_bounds__(kLongThreads) void topk_compact_kernel(
   const int nch = (n + kChunk - 1) / kChunk;
   if (c >= nch) return;
   const float* row = scores + (int64_t)r * ld;
-  const uint32_t theta = hdr[r].theta;
-  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int base = c * kChunk;
   const int end = min(n, base + kChunk);
   constexpr int per = kChunk / NW;
   constexpr int kIter = per / WAVE;
   const int wb = base + w * per;
-  // Each lane keeps its keys in registers between the counting and the writing pass.
+  // The chunk's keys stay in registers from here to the compaction.
   uint32_t key[kIter];
-  int cnt = 0;
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
     const int e = wb + it * WAVE + lane;
     key[it] = float_key(row[min(e, end - 1)]);  // unconditional: all loads in flight at once
   }
+  {
+    constexpr int kPer = kSample / kLongThreads;
+    uint32_t kv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) kv[u] = float_key(row[(int64_t)(tid + u * kLongThreads) * n / kSample]);
+    uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      samp[tid + u * kLongThreads] = kv[u];
+      lmn = min(lmn, kv[u]);
+      lmx = max(lmx, kv[u]);
+    }
+    publish_range<kLongThreads>(lmn, lmx, hist, st);
+  }
+  __syncthreads();
+  int ks = (int)(((int64_t)2 * k * kSample + n - 1) / n);
+  ks = ks < 1 ? 1 : (ks > kSample ? kSample : ks);
+  // Any sample key of rank ks .. ks + ks/4 serves: the search stops at the first bin that
+  // close, usually after one pass.
+  const Threshold th = find_threshold<kLongThreads, true>(LdsKeys{samp, 0}, kSample, ks, hist, st, ks / 4);
+  // theta = the smallest sample key >= T.  (When the search stops early T is only that
+  // bin's lower bound, and the full row can hold many more scores between T and the
+  // smallest sample in the bin.)
+  uint32_t theta = th.T;
+  if (th.exact) {
+    uint32_t mn = 0xFFFFFFFFu;
+    for (int i = tid; i < kSample; i += kLongThreads) {
+      const uint32_t sk = samp[i];
+      if (sk >= th.T) mn = min(mn, sk);
+    }
+    mn = wave_reduce(mn, UMin{});
+    if (lane == 0) st.wred[w] = mn;  // not wmin: slower waves may still read that
+    __syncthreads();
+    theta = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) theta = min(theta, st.wred[i]);
+  }
+  if (c == 0 && tid == 0) {
+    // Survivor bins span [theta, largest sample] in at most kSurvBins steps of 2^shift;
+    // scores above the largest sample land in the last bin.
+    const uint32_t width = th.top - theta;
+    const int shift = width ? max(0, 32 - __builtin_clz(width) - 12) : 0;
+    hdr[r] = RowHeader{theta, (uint32_t)shift};
+  }
+  int cnt = 0;
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
     const int e = wb + it * WAVE + lane;
     cnt += __popcll(ballot(e < end && key[it] >= theta));
   }
-  if (lane == 0) wtot[w] = cnt;
+  if (lane == 0) st.wtot[0][w] = cnt;
   __syncthreads();
   int off = 0;
-  for (int v = 0; v < w; ++v) off += wtot[v];
+  for (int v = 0; v < w; ++v) off += st.wtot[0][v];
   uint2* cr = cand + (int64_t)r * ld + base;
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
@@ -391,31 +446,29 @@ __global__ __launch_bounds__(kLongThreads) void topk_compact_kernel(
     if (keep) cr[off + mask_rank(km)] = make_uint2(key[it], (uint32_t)e);
     off += __popcll(km);
   }
-  if (threadIdx.x == kLongThreads - 1) counts[(int64_t)r * max_chunks + c] = (uint32_t)off;
+  if (tid == kLongThreads - 1) counts[(int64_t)r * max_chunks + c] = (uint32_t)off;
 }
 
 // Long rows, pass 2 (one workgroup per row): exact top-k among the survivors in LDS, or
-// among the whole row when the sample threshold kept fewer than k or more than fit.
-__global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
-    int32_t* __restrict__ idx, const uint32_t* __restrict__ counts, int max_chunks,
-    const uint2* __restrict__ cand) {
-  extern __shared__ uint32_t smem[];  // [kCandCap] keys, [kCandCap] ids, [max_chunks + 1] offsets
-  __shared__ int hist[2 * kHistBins];
-  __shared__ SelState st;
+// among the whole row when the sample threshold kept fewer than k or more than fit.  The
+// survivors are histogrammed into kSurvBins bins above theta as they are gathered, so the
+// bin holding the k-th largest is found by one block scan; the keys of that bin are then
+// ranked directly, or by the radix select when there are too many of them.
+__device__ void resolve_long_row(const float* __restrict__ row, int ld, int n, int k, int r,
+                                 int32_t* __restrict__ out, const RowHeader* __restrict__ hdr,
+                                 const uint32_t* __restrict__ counts, int max_chunks,
+                                 const uint2* __restrict__ cand, uint32_t* smem, int* hist,
+                                 uint2* ties, SelState& st) {
+  static_assert(kSurvBins <= kPassMax * kHistBins, "the survivor histogram reuses the radix buffers");
+  static_assert(kSurvBins == 4 * kResolveThreads, "four survivor bins per thread");
   constexpr int NW = kResolveThreads / WAVE;
-  const int r = blockIdx.x;
-  int64_t n64 = n_valid[r];
-  n64 = n64 < 0 ? 0 : (n64 > ld ? ld : n64);
-  const int n = (int)n64;
-  if (n <= kRowMax || n <= k) return;
   const int nch = (n + kChunk - 1) / kChunk;
-  const float* row = scores + (int64_t)r * ld;
   uint32_t* keys = smem;
   int* ids = reinterpret_cast<int*>(smem + kCandCap);
   int* offs = reinterpret_cast<int*>(smem + 2 * kCandCap);
   const uint32_t* rc = counts + (int64_t)r * max_chunks;
-  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const RowHeader rh = hdr[r];
   if (w == 0) {  // exclusive prefix of the survivor counts, 64 chunks per step
     int carry = 0;
     for (int j0 = 0; j0 < nch; j0 += WAVE) {
@@ -427,10 +480,17 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
     }
     if (lane == 0) offs[nch] = carry;
   }
+  reinterpret_cast<int4*>(hist)[tid] = make_int4(0, 0, 0, 0);
+  if (tid == 0) st.ntie = 0;
   __syncthreads();
   const int total = offs[nch];
-  int32_t* out = idx + (int64_t)r * k;
-  if (total >= k && total <= kCandCap) {
+  if (total < k || total > kCandCap) {
+    const GlobalRow src{row};
+    const Threshold th = find_threshold<kResolveThreads>(src, n, k, hist, st);
+    emit_selected<kResolveThreads>(src, n, th, st, out);
+    return;
+  }
+  {
     // Wave w copies chunks w, w + NW, ...; each lane issues up to U loads per chunk group
     // before storing, so typical chunks (~2k/32 survivors) cost one round trip.
     const uint2* rcand = cand + (int64_t)r * ld;
@@ -447,19 +507,118 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
           if (i < cj) {
             keys[o + i] = v[u].x;
             ids[o + i] = (int)v[u].y;
+            atomicAdd(&hist[min((v[u].x - rh.theta) >> rh.shift, (uint32_t)(kSurvBins - 1))], 1);
           }
         }
       }
     }
-    __syncthreads();
-    const LdsPairs src{keys, ids};
-    const Threshold th = find_threshold<kResolveThreads>(src, total, k, hist, st);
-    emit_selected<kResolveThreads>(src, total, th, st, out);
-  } else {
-    const GlobalRow src{row};
-    const Threshold th = find_threshold<kResolveThreads>(src, n, k, hist, st);
-    emit_selected<kResolveThreads>(src, n, th, st, out);
   }
+  __syncthreads();
+  // Bin b* of the k-th largest survivor: thread t holds bins 4095-4t .. 4092-4t (top down);
+  // every wave then finds the crossing wave from the per-wave totals and rescans its bins.
+  const int4 hv = reinterpret_cast<const int4*>(hist)[kResolveThreads - 1 - tid];
+  const int incl = wave_incl_scan(hv.x + hv.y + hv.z + hv.w);
+  if (lane == WAVE - 1) st.wscan[w] = incl;
+  __syncthreads();
+  int before = 0, vc = -1;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const int tv = st.wscan[v];
+    const bool hit = vc < 0 && before + tv >= k;
+    before += (vc < 0 && !hit) ? tv : 0;
+    vc = hit ? v : vc;
+  }
+  const int4 hc = reinterpret_cast<const int4*>(hist)[kResolveThreads - 1 - (vc * WAVE + lane)];
+  const int cb[4] = {hc.w, hc.z, hc.y, hc.x};
+  int bstar, above, bcnt;
+  wave_crossing<4>(cb, kSurvBins - 1 - 4 * (vc * WAVE + lane), before, k, bstar, above, bcnt);
+  const int need = k - above;
+  const uint32_t t_lo = rh.theta + ((uint32_t)bstar << rh.shift);  // first key of bin b*
+  const LdsPairs src{keys, ids};
+  Threshold th;
+  if (bcnt == need) {
+    th = Threshold{t_lo, 0, true, 0u};  // all of bin b* and above: { key >= t_lo }
+  } else if (bcnt <= kTieMax) {
+    // Rank the keys of bin b* by (key descending, position ascending); the one of rank
+    // need-1 is the threshold T, and need - (keys of the bin above T) of those equal to T
+    // are taken, lowest position first -- the same rule the emit pass applies.
+    const uint64_t bin_end = (uint64_t)t_lo + ((uint64_t)1 << rh.shift) - 1;  // may pass 2^32
+    const uint32_t t_hi = (bstar == kSurvBins - 1 || bin_end > 0xFFFFFFFFull) ? 0xFFFFFFFFu : (uint32_t)bin_end;
+    for (int i0 = 0; i0 < total; i0 += kResolveThreads * 4) {
+      uint32_t kv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kv[u] = keys[min(i0 + u * kResolveThreads + tid, total - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kResolveThreads + tid;
+        const bool in = (i < total) & (kv[u] >= t_lo) & (kv[u] <= t_hi);
+        const uint64_t im = ballot(in);
+        if (im) {  // one slot reservation per wave and round
+          int slot = 0;
+          if (lane == 0) slot = atomicAdd(&st.ntie, __popcll(im));
+          slot = readlane(slot, 0);
+          if (in) ties[slot + mask_rank(im)] = make_uint2(kv[u], (uint32_t)i);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < bcnt) {
+      const uint2 me = ties[tid];
+      int gt = 0, eq_before = 0;
+      for (int j = 0; j < bcnt; ++j) {
+        const uint2 o = ties[j];
+        gt += o.x > me.x;
+        eq_before += (o.x == me.x) & (o.y < me.y);
+      }
+      if (gt + eq_before == need - 1) {
+        st.tie_T = me.x;
+        st.tie_need = need - gt;
+      }
+    }
+    __syncthreads();
+    th = Threshold{st.tie_T, st.tie_need, false, 0u};
+  } else {
+    __syncthreads();  // every wave has read the survivor histogram before the radix select clears it
+    th = find_threshold<kResolveThreads>(src, total, k, hist, st);
+  }
+  emit_selected<kResolveThreads>(src, total, th, st, out);
+}
+
+// One workgroup per row: trivial rows, LDS-resident rows, or the resolve of long rows.
+__global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
+    int32_t* __restrict__ idx, const RowHeader* __restrict__ hdr, const uint32_t* __restrict__ counts,
+    int max_chunks, const uint2* __restrict__ cand) {
+  static_assert(kRowThreads == kResolveThreads, "one kernel serves both paths");
+  extern __shared__ uint32_t smem[];  // row keys, or survivor keys, ids and chunk offsets
+  __shared__ __attribute__((aligned(16))) int hist[kPassMax * kHistBins];
+  __shared__ uint2 ties[kTieMax];
+  __shared__ SelState st;
+  const int r = blockIdx.x;
+  int64_t n64 = n_valid[r];
+  n64 = n64 < 0 ? 0 : (n64 > ld ? ld : n64);
+  const int n = (int)n64;
+  int32_t* out = idx + (int64_t)r * k;
+  const float* row = scores + (int64_t)r * ld;
+  if (n <= k) {
+    for (int i = threadIdx.x; i < k; i += kRowThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  if (n <= kRowMax) {
+    uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
+    for_each_key<kRowThreads, 16>(GlobalRow{row}, n, [&](int i, uint32_t key) {
+      smem[i] = key;
+      lmn = min(lmn, key);
+      lmx = max(lmx, key);
+    });
+    publish_range<kRowThreads>(lmn, lmx, hist, st);
+    __syncthreads();
+    const LdsKeys src{smem, 0};
+    const Threshold th = find_threshold<kRowThreads, true>(src, n, k, hist, st);
+    emit_selected<kRowThreads>(src, n, th, st, out);
+    return;
+  }
+  resolve_long_row(row, (int)ld, n, k, r, out, hdr, counts, max_chunks, cand, smem, hist, ties, st);
 }
 
 struct WsLayout {
@@ -491,19 +650,18 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, 
   const WsLayout L = ws_layout(R, ld);
   char* wsb = static_cast<char*>(ws);
   RowHeader* hdr = L.total ? reinterpret_cast<RowHeader*>(wsb + L.hdr) : nullptr;
-  const size_t row_lds = sizeof(uint32_t) * (size_t)(ld < kRowMax ? (ld > kSample ? ld : kSample) : kRowMax);
-  topk_rows_kernel<<<R, kRowThreads, row_lds, s>>>(scores, ld, n_valid, k, idx, hdr);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || L.total == 0) return e;
-  uint32_t* counts = reinterpret_cast<uint32_t*>(wsb + L.counts);
-  uint2* cand = reinterpret_cast<uint2*>(wsb + L.cand);
-  topk_compact_kernel<<<dim3(R, L.max_chunks), kLongThreads, 0, s>>>(scores, ld, n_valid, k, hdr, counts,
-                                                                     L.max_chunks, cand);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t long_lds = sizeof(uint32_t) * (2 * (size_t)kCandCap + L.max_chunks + 1);
-  topk_resolve_kernel<<<R, kResolveThreads, long_lds, s>>>(scores, ld, n_valid, k, idx, counts, L.max_chunks,
-                                                        cand);
+  uint32_t* counts = L.total ? reinterpret_cast<uint32_t*>(wsb + L.counts) : nullptr;
+  uint2* cand = L.total ? reinterpret_cast<uint2*>(wsb + L.cand) : nullptr;
+  if (L.total) {
+    topk_prep_kernel<<<dim3(R, L.max_chunks), kLongThreads, 0, s>>>(scores, ld, n_valid, k, hdr, counts,
+                                                                  L.max_chunks, cand);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const size_t row_lds = sizeof(uint32_t) * (size_t)(ld < kRowMax ? ld : kRowMax);
+  const size_t long_lds = L.total ? sizeof(uint32_t) * (2 * (size_t)kCandCap + L.max_chunks + 1) : 0;
+  topk_finish_kernel<<<R, kRowThreads, row_lds > long_lds ? row_lds : long_lds, s>>>(
+      scores, ld, n_valid, k, idx, hdr, counts, L.max_chunks, cand);
   return hipGetLastError();
 }
 

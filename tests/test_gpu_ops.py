@@ -172,6 +172,32 @@ def test_topk_long_rows_sample_misses_survivors():
     _expect_topk(s, [ld], k, got)
 
 
+def test_topk_long_rows_boundary_bin():
+    _case("topk long rows, ties and crowding in the boundary bin")
+    # Quantised scores put several equal keys in the histogram bin that holds the k-th
+    # largest survivor: few (pairwise ranking), dozens (still ranked), hundreds (radix
+    # select over the survivors).  The last two rows put large scores only at positions the
+    # sample never reads, so the boundary falls in the histogram's open-ended top bin.
+    rng = np.random.default_rng(35)
+    ld, k = 131072, 2048
+    s = rng.standard_normal((6, ld)).astype(np.float32)
+    s[0] = np.round(s[0] * 512) / 512
+    s[1] = np.round(s[1] * 64) / 64
+    s[2] = np.round(s[2] * 16) / 16
+    sample = (np.arange(2048) * ld) // 2048
+    off_sample = np.setdiff1d(np.arange(ld), sample)
+    for r, m in ((3, 3000), (4, 2100)):
+        s[r] = rng.uniform(0, 1, ld)
+        s[r, rng.choice(off_sample, m, replace=False)] = rng.uniform(5, 6, m)
+    s[5] = rng.uniform(0, 1, ld)
+    s[5, rng.choice(off_sample, 200, replace=False)] = np.round(rng.uniform(5, 6, 200) * 8) / 8
+    n_valid = [ld, 120000, ld, ld, ld, ld]
+    got = _run_topk(s, n_valid, k)
+    _expect_topk(s, n_valid, k, got)
+    got = _run_topk(s[5:], [ld], 100)                      # boundary in the top bin, ties ranked
+    _expect_topk(s[5:], [ld], 100, got)
+
+
 # ----------------------------------------------------------------------------- sparse MLA
 def _random_sets(rng, lengths, k, holes=True):
     B = len(lengths)
