@@ -31,16 +31,17 @@ constexpr int kDv = 512;
 constexpr int kTok = 32;                        // rows per LDS tile
 constexpr int kRowChunks = kDqk * 2 / 16;       // 72 16-byte chunks per latent row
 constexpr int kDmaPerTile = kRowChunks / 2;     // 36 wave-wide 1 KB copies per tile
-// Tile layout (chunk-major): copy j fills block j with chunk j of rows 0..31 (lanes 0-31)
-// and chunk j + 36 (lanes 32-63), 16 bytes per lane.  Blocks are 1088 bytes apart so
-// chunks 2d and 2d+1 (one 16-column value slice) sit 16 banks apart for the transposing
-// reads; a 16-lane read of one chunk covers 256 contiguous bytes (all 64 banks).
-constexpr int kBlock = 1024 + 64;
-constexpr int kBufBytes = kDmaPerTile * kBlock;  // 39168
+// Tile layout (chunk-major): copy j fills block j with chunk j of rows 0..31 (lanes 0-31,
+// "side 0") and chunk j + 36 (lanes 32-63, "side 1"), 16 bytes per lane.  With 1024-byte
+// blocks the logit-fragment reads (16 rows of one chunk per 16 lanes, four chunks per
+// wave) are free of bank conflicts on gfx950; the transposing value reads run at their
+// own rate with either this or a padded stride (both measured).
+constexpr int kBlock = 1024;
+constexpr int kBufBytes = kDmaPerTile * kBlock;  // 36864
 constexpr int kNBuf = 3;                        // ring depth: two tiles in flight during compute
-constexpr int kMlaWaves = 4;                    // compute waves, 16 heads each
-constexpr int kMlaThreads = (kMlaWaves + 1) * WAVE;          // + one loader wave
-constexpr int kHeadsPerWg = 16 * kMlaWaves;
+constexpr int kMlaWaves = 8;                    // compute waves: two per 16-head block
+constexpr int kMlaThreads = (kMlaWaves + 1) * WAVE;  // + one copy wave
+constexpr int kHeadsPerWg = 64;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // Byte offset of (row, 16-byte chunk c) inside a tile.
@@ -50,8 +51,12 @@ __device__ __forceinline__ int tile_off(int row, int c) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// LDS pointers are formed from the byte offset, which a flat pointer into LDS carries in
+// its low 32 bits: a flat-to-LDS pointer cast would add a null check per use.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)p; }
+
 __device__ __forceinline__ v4bf lds_read_tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(p));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(uintptr_t)lds_offset(p));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (expcnt, lgkmcnt left at max).
@@ -61,14 +66,42 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-__shared__ __attribute__((aligned(16))) char g_ring[kNBuf][kBufBytes];
+// The ring's three slots are separate LDS variables, so the compiler can tell that a copy
+// into one slot never aliases the reads of another and puts no wait between them.
+__shared__ __attribute__((aligned(16))) char g_ring0[kBufBytes];
+__shared__ __attribute__((aligned(16))) char g_ring1[kBufBytes];
+__shared__ __attribute__((aligned(16))) char g_ring2[kBufBytes];
+// Partial logits exchanged between the two waves of a head block (8 floats per lane).
+__shared__ __attribute__((aligned(16))) float g_xchg[kMlaWaves][WAVE * 8];
 
-// One workgroup = (row r, 64 heads, a range of the kept set).  Wave 4 is the loader: it
-// streams each 32-row tile straight from global memory into a 3-deep LDS ring with
-// global_load_lds_dwordx4 (a row is gathered once and shared by all 64 heads) and never
-// reads the ring, so its copies stay in flight across the tile barriers; waves 0-3
-// compute.  The loader's only LDS reads are the row list `srow`, a different LDS array,
-// which keeps the compiler from waiting on the copies before them.
+template <int S>
+__device__ __forceinline__ char* ring_slot() {
+  static_assert(S >= 0 && S < kNBuf, "ring slot");
+  return S == 0 ? g_ring0 : (S == 1 ? g_ring1 : g_ring2);
+}
+template <int S>
+struct Slot {
+  static constexpr int value = S;
+};
+
+// One workgroup = (row r, 64 heads, a range of the kept set): eight compute waves and one
+// copy wave.  Compute waves w and w+4 share head block w&3 (16 heads): for S^T = K Q^T each
+// takes one half of the 576 latent columns and the two partial logit tiles are summed
+// through LDS (both waves then hold identical logits and run identical softmax
+// statistics); for O^T += V^T P^T each takes one half of the 512 value columns.  Per wave
+// that is half the query fragments and half the output accumulators of a whole-head-block
+// wave, which leaves registers for LDS prefetch at three waves per SIMD.
+//
+// The copy wave streams each 32-row tile straight from global memory into a 3-deep LDS
+// ring with global_load_lds_dwordx4 (a row is gathered once and shared by all 64 heads),
+// two tiles ahead of the one being computed, and hands a tile over by waiting for its
+// copies and one barrier (it also takes part in the compute waves' second barrier of each
+// tile, the logit exchange, so the two sides' barriers pair up).  It starts the first two tiles from the split's first 64
+// indices before building the rest of the row list, so the first gather overlaps the
+// query loads.  It never reads the ring (its only LDS reads are the row list, a different
+// variable), so the compiler never waits on copies in flight; the compute waves issue no
+// copies.  The tile loop is unrolled by the ring depth so every slot is a compile-time
+// LDS variable.
 template <bool PAGED, bool SPLIT>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -76,8 +109,8 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     const int32_t* __restrict__ idx, int k, int H, int decode, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml, int n_split, int tok_per_split) {
-  extern __shared__ int srow[];  // [tok_per_split] cache row of each kept token, -1 = none
-
+  extern __shared__ int srow[];  // [tok_per_split] cache row of each kept token, -1 = none;
+                                 // then [tiles] bit mask of each tile's live tokens
   const int HG = H / kHeadsPerWg;
   int bid = blockIdx.x;
   const int sp = bid % n_split;
@@ -87,110 +120,175 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   const int t_begin = sp * tok_per_split;
   const int t_end = min(k, t_begin + tok_per_split);
   const int n_tok = t_end > t_begin ? t_end - t_begin : 0;
+  const int ntiles = (n_tok + kTok - 1) / kTok;
   const int seq = decode ? r : 0;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const int32_t* irow = idx + (int64_t)r * k + t_begin;
-  // Rows are addressed relative to `base`: the sequence's first row (contiguous) or the
-  // pool (paged: the page table is resolved here, once per kept token).
-  const uint16_t* base = PAGED ? kv : kv + (int64_t)seq * seq_stride * kDqk;
-  // Query fragments of the compute waves, issued before the row list is built so the two
-  // latencies overlap: B[k = dim][n = head col] = q[r, h, 32*kk + 8*grp + j].
-  const int col = lane & 15, grp = lane >> 4;
-  const int h = hg * kHeadsPerWg + 16 * min(w, kMlaWaves - 1) + col;
-  const uint16_t* qrow = q + ((int64_t)r * H + h) * kDqk;
-  v8bf qf[kDqk / 32];
-  if (w < kMlaWaves) {
-    const uint4* qp = reinterpret_cast<const uint4*>(qrow + 8 * grp);
-#pragma unroll
-    for (int kk = 0; kk < kDqk / 32; ++kk) {
-      const uint4 x = qp[4 * kk];
-      qf[kk] = __builtin_bit_cast(v8bf, x);
-    }
-  }
-  {
-    constexpr int U = 8;  // ids (and their page-table entries) read in batches
-    for (int i0 = 0; i0 < n_tok; i0 += U * kMlaThreads) {
-      int id[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * kMlaThreads + tid;
-        const int v = irow[min(i, n_tok - 1)];  // unconditional load: no wait between batch members
-        id[u] = i < n_tok ? v : -1;
-      }
-      if (PAGED) {
-        int pg[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          pg[u] = table[(int64_t)seq * max_pages + (id[u] >= 0 ? id[u] : 0) / page_size];
-#pragma unroll
-        for (int u = 0; u < U; ++u) id[u] = id[u] >= 0 ? pg[u] * page_size + id[u] % page_size : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * kMlaThreads + tid;
-        if (i < n_tok) srow[i] = id[u] >= 0 ? id[u] : -1;
-      }
-    }
-  }
-  __syncthreads();
-  const int ntiles = (n_tok + kTok - 1) / kTok;
+  uint32_t* smask = reinterpret_cast<uint32_t*>(srow + tok_per_split);
 
   if (w == kMlaWaves) {
-    // ---------------------------------------------------------------- loader wave
+    // ---------------------------------------------------------------- copy wave
+    const int32_t* irow = idx + (int64_t)r * k + t_begin;
+    // Rows are addressed relative to `base`: the sequence's first row (contiguous) or the
+    // pool (paged: the page table is resolved here, once per kept token).
+    const uint16_t* base = PAGED ? kv : kv + (int64_t)seq * seq_stride * kDqk;
+    auto resolve = [&](int id) -> int {  // cache row of a token index (-1 stays -1)
+      if (!PAGED) return id;
+      const int pg = table[(int64_t)seq * max_pages + (id >= 0 ? id : 0) / page_size];
+      return id >= 0 ? pg * page_size + id % page_size : -1;
+    };
     // Dead rows (past the range or index -1) copy this row's first query row, which is
     // finite, so masked tokens never inject NaN into the value products.
     const uint16_t* dummy = q + (int64_t)r * H * kDqk;
     const int half = lane >> 5;  // lanes 32-63 copy the row's second half (chunks 36..71)
-    auto issue = [&](int t) {
-      char* dst = g_ring[t % kNBuf];
-      const int tok = t * kTok + (lane & 31);
-      const int row = tok < n_tok ? srow[tok] : -1;
+    auto issue_row = [&](int row, char* dst) {
       const uint16_t* src = (row >= 0 ? base + (int64_t)row * kDqk : dummy) + half * (kDqk / 2);
 #pragma unroll
       for (int j = 0; j < kDmaPerTile; ++j)
-        __builtin_amdgcn_global_load_lds((const void*)(src + 8 * j), (lds_void*)(dst + j * kBlock), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(src + 8 * j),
+                                         (lds_void*)(uintptr_t)(lds_offset(dst) + j * kBlock), 16, 0, 0);
     };
-    if (ntiles > 0) issue(0);
-    if (ntiles > 1) issue(1);
-    for (int t = 0; t < ntiles; ++t) {
+    // Tiles 0 and 1 straight from the first 64 indices (token = lane).
+    {
+      const int v = lane < n_tok ? irow[min(lane, n_tok - 1)] : -1;
+      const int row = resolve(v);
+      const uint64_t live = ballot(row >= 0);
+      if (lane < n_tok) srow[lane] = row;
+      if (lane == 0) {
+        if (ntiles > 0) smask[0] = (uint32_t)live;
+        if (ntiles > 1) smask[1] = (uint32_t)(live >> 32);
+      }
+      // lane l needs token l & 31 (tile 0) and 32 + (l & 31) (tile 1)
+      const v2i sw = __builtin_amdgcn_permlane32_swap(row, row, false, false);
+      if (ntiles > 0) issue_row(sw[0], g_ring0);
+      if (ntiles > 1) issue_row(sw[1], g_ring1);
+    }
+    // The rest of the row list, 8 tokens per lane per batch.
+    constexpr int U = 8;
+    for (int i0 = 64; i0 < n_tok; i0 += U * WAVE) {
+      int id[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * WAVE + lane;
+        const int v = irow[min(i, n_tok - 1)];  // unconditional load: no wait between batch members
+        id[u] = i < n_tok ? v : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * WAVE + lane;
+        const int row = resolve(id[u]);
+        const uint64_t live = ballot(row >= 0);
+        if (i < n_tok) srow[i] = row;
+        const int t0 = (i0 + u * WAVE) / kTok;
+        if (lane == 0 && t0 < ntiles) smask[t0] = (uint32_t)live;
+        if (lane == 0 && t0 + 1 < ntiles) smask[t0 + 1] = (uint32_t)(live >> 32);
+      }
+    }
+    auto row_of_tile = [&](int t) {
+      const int tok = t * kTok + (lane & 31);
+      return tok < n_tok ? srow[tok] : -1;
+    };
+    auto hand = [&](auto slot, int t) {
+      constexpr int S = decltype(slot)::value;
       if (t + 1 < ntiles) wait_vmcnt<kDmaPerTile>();  // tile t landed, t+1 may be in flight
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();                    // hand tile t to the compute waves
-      if (t + 2 < ntiles) issue(t + 2);                // its buffer was freed by tile t-1
+      if (t + 2 < ntiles) issue_row(row_of_tile(t + 2), ring_slot<(S + 2) % kNBuf>());
+      __builtin_amdgcn_s_barrier();  // the compute waves' logit exchange (barriers must pair up)
+    };
+    for (int t = 0; t < ntiles; t += kNBuf) {
+      hand(Slot<0>{}, t);
+      if (t + 1 < ntiles) hand(Slot<1>{}, t + 1);
+      if (t + 2 < ntiles) hand(Slot<2>{}, t + 2);
     }
     return;
   }
 
   // ------------------------------------------------------------------ compute waves
-  v4f acc_o[kDv / 16];
+  const int hb = w & 3;     // head block
+  const int half = w >> 2;  // latent-column half (logits) and value-column half (output)
+  // Query fragments of this wave's column half: B[k = dim][n = head col] =
+  // q[r, h, 288*half + 32*kk + 8*grp + j].
+  constexpr int kKK = kDqk / 64;  // 9 steps of 32 columns per half
+  const int col = lane & 15, grp = lane >> 4;
+  const int h = hg * kHeadsPerWg + 16 * hb + col;
+  const uint16_t* qrow = q + ((int64_t)r * H + h) * kDqk + (kDqk / 2) * half;
+  v8bf qf[kKK];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(qrow + 8 * grp);
 #pragma unroll
-  for (int dt = 0; dt < kDv / 16; ++dt) acc_o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < kKK; ++kk) qf[kk] = __builtin_bit_cast(v8bf, qp[4 * kk]);
+  }
+  constexpr int kVSide1 = 14;  // half 1: value tiles below this are on side 1
+  v4f acc_o[kDv / 32];         // value tile dt of this half (columns in the epilogue), head col
+#pragma unroll
+  for (int dt = 0; dt < kDv / 32; ++dt) acc_o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;  // reference max of scaled logits (log2 domain), per head = col
   float l_run = 0.0f;       // this lane's share of the running sum
+  // Logit fragments: chunk 36*half + 4*kk + grp of row 16*st + col sits in block 4*kk + grp,
+  // side `half` (tile layout above), so every fragment is this lane base plus a constant.
+  const int qk_lane = grp * kBlock + 512 * half + 16 * col;
+  // Value fragments.  Value-column tile dt (16 columns, chunks 2dt' and 2dt'+1 of the row)
+  // is read by a transposing load where lane (col, grp) supplies row 4*grp + col/4 (+16),
+  // columns +4*(col&3) .. +3: chunk +(col&3)/2, byte 8*(col&1).  Half 0 takes chunks 0..31
+  // (side 0, blocks 0..31); half 1 takes chunks 36..63 (side 1, blocks 0..27) as its tiles
+  // 0..13 and chunks 32..35 (side 0, blocks 32..35) as tiles 14 and 15.  Both are a lane
+  // base plus a constant per tile.
+  const int pv_lane = ((col & 3) >> 1) * kBlock + 16 * (4 * grp + (col >> 2)) + 8 * (col & 1);
+  const int pv_lane_a = pv_lane + 512 * half;            // tiles 0..13
+  const int pv_lane_b = pv_lane + (half ? 4 * kBlock : 0);  // tiles 14, 15
+  float* xmine = &g_xchg[w][lane * 8];
+  const float* xpart = &g_xchg[w ^ 4][lane * 8];
 
-  for (int t = 0; t < ntiles; ++t) {
-    __builtin_amdgcn_s_barrier();  // tile t is in g_ring[t % kNBuf]
-    const char* tb = g_ring[t % kNBuf];
-    // ---- S^T = K Q^T for tokens 0..15 (st = 0) and 16..31 (st = 1)
-    v4f acc_s[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+  auto step = [&](auto slot, int t) {
+    constexpr int S = decltype(slot)::value;
+    __builtin_amdgcn_s_barrier();  // tile t is in ring slot S
+    const char* tb = ring_slot<S>();
+    // ---- partial S^T over this wave's 288 columns: tokens 16*st + row, two accumulation
+    // chains (one per token half), KD K fragments in flight.
+    constexpr int NF = 2 * kKK;
+    constexpr int KD = 4;
+    const char* kb = tb + qk_lane;
+    auto kfrag = [&](int i) {
+      return *reinterpret_cast<const v8bf*>(kb + (i >> 1) * 4 * kBlock + (i & 1) * 256);
+    };
+    v8bf kf[KD];
 #pragma unroll
-    for (int kk = 0; kk < kDqk / 32; ++kk) {
+    for (int i = 0; i < KD; ++i) kf[i] = kfrag(i);
+    v4f as[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const v8bf a = *reinterpret_cast<const v8bf*>(tb + tile_off(16 * st + col, 4 * kk + grp));
-        acc_s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], acc_s[st], 0, 0, 0);
-      }
+    for (int i = 0; i < NF; ++i) {
+      const v8bf a = kf[i % KD];
+      if (i + KD < NF) kf[i % KD] = kfrag(i + KD);
+      as[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i >> 1], as[i & 1], 0, 0, 0);
     }
+    // (Compute waves issue no copies, so these stores wait on nothing in flight.)
+    *reinterpret_cast<v4f*>(xmine) = as[0];
+    *reinterpret_cast<v4f*>(xmine + 4) = as[1];
+    // First value fragments, read while the partner's logits arrive.
+    constexpr int VD = 3;
+    v4bf vlo[VD], vhi[VD];
+    auto vfrag = [&](int dt, v4bf& lo, v4bf& hi) {
+      const char* vb = tb + (dt < kVSide1 ? pv_lane_a : pv_lane_b) + dt * 2 * kBlock;
+      lo = lds_read_tr16(vb);
+      hi = lds_read_tr16(vb + 16 * 16);
+    };
+#pragma unroll
+    for (int d = 0; d < VD; ++d) vfrag(d, vlo[d], vhi[d]);
+    __syncthreads();  // both halves of every logit tile are in LDS
+    const v4f p0 = *reinterpret_cast<const v4f*>(xpart);
+    const v4f p1 = *reinterpret_cast<const v4f*>(xpart + 4);
+    // Both waves of a pair add the same two halves (a + b == b + a), so their logits agree.
+    const v4f sf[2] = {as[0] + p0, as[1] + p1};
     // ---- online softmax (lane holds tokens 16*st + 4*grp + i of head col)
+    const uint32_t live = smask[t];
     float s[2][4];
     float mx = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = t * kTok + 16 * st + 4 * grp + i;
-        const bool ok = tok < n_tok && srow[tok] >= 0;
-        s[st][i] = ok ? acc_s[st][i] * scale_log2 : -INFINITY;
+        const bool ok = (live >> (16 * st + 4 * grp + i)) & 1u;
+        s[st][i] = ok ? sf[st][i] * scale_log2 : -INFINITY;
         mx = fmaxf(mx, s[st][i]);
       }
     }
@@ -201,10 +299,10 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     float m_ref = m_run;
     if (__ballot(mx > m_run + 8.0f)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
+      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < kDv / 16; ++dt) acc_o[dt] *= alpha;
+      for (int dt = 0; dt < kDv / 32; ++dt) acc_o[dt] *= alpha;
       m_ref = m_new;
     }
     m_run = m_ref;
@@ -215,7 +313,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[st][i] = exp2f(s[st][i] - m_use);
+        p[st][i] = __builtin_amdgcn_exp2f(s[st][i] - m_use);
         psum += p[st][i];
       }
     }
@@ -227,43 +325,48 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
       pf[i] = (__bf16)p[0][i];
       pf[4 + i] = (__bf16)p[1][i];
     }
-    // ---- O^T += V^T P^T, 32 tiles of 16 value columns
-    // lane (col, grp) of a transposing read supplies row 4*grp + col/4 (+16), value columns
-    // 16*dt + 4*(col&3) .. +3: chunk 2*dt + (col&3)/2, byte 8*(col&1) within it.
-    const int vrow = 4 * grp + (col >> 2);
-    const int vsub = 8 * (col & 1);
+    // ---- O^T += V^T P^T over this wave's 16 tiles of 16 value columns
 #pragma unroll
-    for (int dt = 0; dt < kDv / 16; ++dt) {
-      const int c = 2 * dt + ((col & 3) >> 1);
-      const v4bf lo = lds_read_tr16(tb + tile_off(vrow, c) + vsub);
-      const v4bf hi = lds_read_tr16(tb + tile_off(vrow + 16, c) + vsub);
-      const v8bf a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int dt = 0; dt < kDv / 32; ++dt) {
+      const v8bf a = __builtin_shufflevector(vlo[dt % VD], vhi[dt % VD], 0, 1, 2, 3, 4, 5, 6, 7);
+      if (dt + VD < kDv / 32) vfrag(dt + VD, vlo[dt % VD], vhi[dt % VD]);
       acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, acc_o[dt], 0, 0, 0);
     }
+  };
+
+  for (int t = 0; t < ntiles; t += kNBuf) {
+    step(Slot<0>{}, t);
+    if (t + 1 < ntiles) step(Slot<1>{}, t + 1);
+    if (t + 2 < ntiles) step(Slot<2>{}, t + 2);
   }
 
   float l = l_run + __shfl_xor(l_run, 16);
   l += __shfl_xor(l, 32);
+  // First value column of this lane in tile dt: half 0 tile dt = columns 16*dt; half 1
+  // tiles 0..13 = columns 288 + 16*dt, tiles 14, 15 = columns 256 + 16*(dt - 14).
+  auto vcol = [&](int dt) {
+    return 4 * grp + (half == 0 ? 16 * dt : (dt < kVSide1 ? 288 + 16 * dt : 256 + 16 * (dt - kVSide1)));
+  };
   if (SPLIT) {
     const int64_t pr = ((int64_t)r * n_split + sp) * H + h;
-    float* po = part_o + pr * kDv + 4 * grp;
+    float* po = part_o + pr * kDv;
 #pragma unroll
-    for (int dt = 0; dt < kDv / 16; ++dt)
-      *reinterpret_cast<float4*>(po + 16 * dt) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
-    if (grp == 0) {
+    for (int dt = 0; dt < kDv / 32; ++dt)
+      *reinterpret_cast<float4*>(po + vcol(dt)) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+    if (grp == 0 && half == 0) {
       part_ml[2 * pr] = m_run;
       part_ml[2 * pr + 1] = l;
     }
   } else {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    uint16_t* op = out + ((int64_t)r * H + h) * kDv + 4 * grp;
+    uint16_t* op = out + ((int64_t)r * H + h) * kDv;
 #pragma unroll
-    for (int dt = 0; dt < kDv / 16; ++dt) {
+    for (int dt = 0; dt < kDv / 32; ++dt) {
       const uint32_t lo = f32_to_bf16(acc_o[dt][0] * inv) | ((uint32_t)f32_to_bf16(acc_o[dt][1] * inv) << 16);
       const uint32_t hi = f32_to_bf16(acc_o[dt][2] * inv) | ((uint32_t)f32_to_bf16(acc_o[dt][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(op + vcol(dt)) = make_uint2(lo, hi);
     }
-    if (lse && grp == 0) lse[(int64_t)r * H + h] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    if (lse && grp == 0 && half == 0) lse[(int64_t)r * H + h] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -381,6 +484,11 @@ __global__ __launch_bounds__(256) void mla_generic_kernel(
   if (lse && tid == 0) lse[(int64_t)r * H + h] = L > 0.0f ? M + logf(L) : -INFINITY;
 }
 
+// Dynamic LDS of the bf16 kernel: the row list and one live-token mask per tile.
+size_t mla_lds_bytes(int tok_per_split) {
+  return sizeof(int) * ((size_t)tok_per_split + (tok_per_split + kTok - 1) / kTok);
+}
+
 struct SplitPlan {
   int n_split, tok_per_split;
 };
@@ -421,7 +529,7 @@ hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o ? part_o + (size_t)R * p.n_split * H * kDv : nullptr;
 #define DSA_MLA_LAUNCH(PG, SP)                                                                   \
-  mla_bf16_kernel<PG, SP><<<grid, kMlaThreads, sizeof(int) * p.tok_per_split, s>>>(q, kvp, kv.table, kv.max_pages,             \
+  mla_bf16_kernel<PG, SP><<<grid, kMlaThreads, mla_lds_bytes(p.tok_per_split), s>>>(q, kvp, kv.table, kv.max_pages,             \
                                                         kv.page_size, kv.seq_stride, idx, k, H,     \
                                                         decode ? 1 : 0, scale_log2, out, lse,       \
                                                         part_o, part_ml, p.n_split, p.tok_per_split)
