@@ -8,18 +8,22 @@
 // section 1).  Row layout (576 = 512 value + 64 rope columns, value = first 512) and the
 // explicit softmax scale are this library's readings.
 //
-// bf16 fast path (Dqk = 576, Dv = 512, 64 heads per workgroup, 4 waves x 16 heads):
+// bf16 fast path (Dqk = 576, Dv = 512, 64 heads per workgroup: four 16-head blocks, each
+// computed by a pair of waves, plus one copy wave):
 //   * 32 selected rows are gathered into LDS once per tile and used by all 64 heads;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = K rows from LDS (ds_read_b128),
-//     B = the wave's 16 query heads held in registers for the whole kernel;
-//     the result layout puts one head per lane column, so the online-softmax row
-//     statistics of a head live in one lane column and need two cross-lane steps;
+//     B = the block's 16 query heads held in registers for the whole kernel (each wave of
+//     the pair holds half of the 576 columns; the two partial logit tiles are summed
+//     through LDS); the result layout puts one head per lane column, so the
+//     online-softmax row statistics of a head live in one lane column and need two
+//     cross-lane steps;
 //   * O^T += V^T P^T: A = V^T fragments read from the row-major LDS tile with the gfx950
 //     transposing LDS load (ds_read_b64_tr_b16), B = P^T straight from the S^T
 //     registers (the token order inside the 32-wide K step is permuted identically on
 //     both operands, so no data moves between lanes);
 //   * decode splits each sequence's kept set over several workgroups and merges the
-//     partial (o, max, sum) triples with a log-sum-exp combine kernel.
+//     partials (each split's normalized output in bf16, its max and sum in fp32) with a
+//     log-sum-exp combine kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ table, int max_pages, int page_size, int64_t seq_stride,
     const int32_t* __restrict__ idx, int k, int H, int decode, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml, int n_split, int tok_per_split) {
   extern __shared__ int srow[];  // [tok_per_split] cache row of each kept token, -1 = none;
                                  // then [tiles] bit mask of each tile's live tokens
@@ -347,18 +351,23 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   auto vcol = [&](int dt) {
     return 4 * grp + (half == 0 ? 16 * dt : (dt < kVSide1 ? 288 + 16 * dt : 256 + 16 * (dt - kVSide1)));
   };
+  // Split partials hold this split's own normalized output (bf16, like the final output)
+  // and its (max, sum) in fp32; the merge weights each by sum * 2^(max - overall max).
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   if (SPLIT) {
     const int64_t pr = ((int64_t)r * n_split + sp) * H + h;
-    float* po = part_o + pr * kDv;
+    uint16_t* po = part_o + pr * kDv;
 #pragma unroll
-    for (int dt = 0; dt < kDv / 32; ++dt)
-      *reinterpret_cast<float4*>(po + vcol(dt)) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+    for (int dt = 0; dt < kDv / 32; ++dt) {
+      const uint32_t lo = f32_to_bf16(acc_o[dt][0] * inv) | ((uint32_t)f32_to_bf16(acc_o[dt][1] * inv) << 16);
+      const uint32_t hi = f32_to_bf16(acc_o[dt][2] * inv) | ((uint32_t)f32_to_bf16(acc_o[dt][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(po + vcol(dt)) = make_uint2(lo, hi);
+    }
     if (grp == 0 && half == 0) {
       part_ml[2 * pr] = m_run;
       part_ml[2 * pr + 1] = l;
     }
   } else {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     uint16_t* op = out + ((int64_t)r * H + h) * kDv;
 #pragma unroll
     for (int dt = 0; dt < kDv / 32; ++dt) {
@@ -371,11 +380,12 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
 }
 
 // Log-sum-exp merge of the split partials: 128 threads per (row, head), 4 value columns
-// per thread.  Splits are taken 16 at a time with every load of a batch (values and the
-// (max, sum) pairs alike) issued before any is used, so a typical merge is one round trip;
-// batches after the first rescale the running sums to the new maximum.
+// per thread.  Split s contributes its normalized output u_s with weight l_s * 2^(m_s - M).
+// Splits are taken 16 at a time with every load of a batch (values and the (max, sum) pairs
+// alike) issued before any is used, so a typical merge is one round trip; batches after the
+// first rescale the running sums to the new maximum.
 constexpr int kCombineBatch = 16;
-__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int RH, int H, int n_split,
                                                           uint16_t* __restrict__ out,
@@ -389,12 +399,12 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
     float2 ml[kCombineBatch];
-    float4 v[kCombineBatch];
+    uint2 v[kCombineBatch];
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u) {
       const int64_t pr = p0 + (int64_t)min(s0 + u, n_split - 1) * H;
       ml[u] = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
-      v[u] = *reinterpret_cast<const float4*>(part_o + pr * kDv + 4 * t);
+      v[u] = *reinterpret_cast<const uint2*>(part_o + pr * kDv + 4 * t);
     }
     float Mb = M;
 #pragma unroll
@@ -406,9 +416,12 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u) {
       const bool valid = s0 + u < n_split && ml[u].y > 0.0f;
-      const float f = valid ? exp2f(ml[u].x - Mb) : 0.0f;
-      L += valid ? ml[u].y * f : 0.0f;
-      acc.x += v[u].x * f; acc.y += v[u].y * f; acc.z += v[u].z * f; acc.w += v[u].w * f;
+      const float f = valid ? ml[u].y * exp2f(ml[u].x - Mb) : 0.0f;
+      L += f;
+      acc.x += __uint_as_float(v[u].x << 16) * f;
+      acc.y += __uint_as_float(v[u].x & 0xFFFF0000u) * f;
+      acc.z += __uint_as_float(v[u].y << 16) * f;
+      acc.w += __uint_as_float(v[u].y & 0xFFFF0000u) * f;
     }
     M = Mb;
   }
@@ -513,7 +526,7 @@ size_t mla_decode_workspace_bytes(int B, int H, int Dv, int k) {
   const SplitPlan p = split_plan(B, H, k);
   if (p.n_split <= 1) return 0;
   const size_t pairs = (size_t)B * p.n_split * H;
-  return pairs * kDv * sizeof(float) + pairs * 2 * sizeof(float);
+  return pairs * kDv * sizeof(uint16_t) + pairs * 2 * sizeof(float);
 }
 
 hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t* idx, int R,
@@ -526,8 +539,8 @@ hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t
   if (p.n_split > 1 && ws_bytes < mla_decode_workspace_bytes(R, H, kDv, k)) return hipErrorInvalidValue;
   if (p.n_split <= 1) p = SplitPlan{1, k};
   const unsigned grid = (unsigned)((int64_t)R * HG * p.n_split);
-  float* part_o = static_cast<float*>(ws);
-  float* part_ml = part_o ? part_o + (size_t)R * p.n_split * H * kDv : nullptr;
+  uint16_t* part_o = static_cast<uint16_t*>(ws);
+  float* part_ml = part_o ? reinterpret_cast<float*>(part_o + (size_t)R * p.n_split * H * kDv) : nullptr;
 #define DSA_MLA_LAUNCH(PG, SP)                                                                   \
   mla_bf16_kernel<PG, SP><<<grid, kMlaThreads, mla_lds_bytes(p.tok_per_split), s>>>(q, kvp, kv.table, kv.max_pages,             \
                                                         kv.page_size, kv.seq_stride, idx, k, H,     \
