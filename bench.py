@@ -1,6 +1,7 @@
 """Benchmark of one DSA decode step at 128k context on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+    python bench.py --mode prefill [--steps K]      (workload 4, reported, not the headline)
 
 A step is the whole hot path for one new token per sequence: dsa_index_scores (FP8
 lightning indexer over every cached token) -> dsa_topk (k = 2048) -> dsa_sparse_mla_decode
@@ -12,6 +13,10 @@ timing starts; `--copies` distinct copies of the caches are rotated step by step
 once per copy in a HIP graph and replayed (the library never allocates or synchronises,
 so capture is plain); an eager pass of the same steps with HIP events around every
 indexer launch gives the indexer's average duration for the roofline figure.
+
+`--mode prefill` times one causal prefill of T = 32768 tokens (workload 4) instead and reports
+the indexer (A2) against the FP8 MFMA peak and the sparse MLA (A6) against the bf16 MFMA peak,
+both as algorithmic flops over each kernel's own event-timed duration.
 
 Prints one JSON line (rank 0, N = 1).  Multi-GPU runs are not part of this build.
 """
@@ -29,6 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0   # dense MFMA, MI355X datasheet
+BF16_PEAK_TFLOPS = 2500.0
 METRIC = "DSA decode tokens/s & us/step at 128k ctx (indexer+top-k+sparse MLA); % roofline"
 
 
@@ -37,6 +44,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--mode", default="decode", choices=["decode", "prefill"])
     p.add_argument("--config", type=int, default=3, choices=[2, 3, 5])
     p.add_argument("--copies", type=int, default=4)
     p.add_argument("--no-graph", action="store_true")
@@ -55,6 +63,8 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "prefill":
+        return prefill(args)
     import numpy as np
     import torch
 
@@ -214,6 +224,76 @@ def main():
                          "eager_step": (te1 - te0) * 1e6 / args.steps},
         "graph_replay_matches_eager": bool(ok),
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def prefill(args):
+    """One causal prefill of workload 4 (T = 32768), each stage timed with HIP events."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import long_context_sparse_06_amd as dsa
+    from datagen.device import upload_prefill
+    from long_context_sparse_06_amd.step import Prefill
+
+    dsa.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = datagen.CONFIGS[4]
+    t0 = time.time()
+    inp = datagen.make_config(4)
+    log(f"[bench] generated {cfg['name']} in {time.time() - t0:.1f}s")
+    sh, T = inp.shapes, inp.T
+    scale = 1.0 / math.sqrt(sh.Dqk)
+    pf = Prefill.from_inputs(upload_prefill(inp, dev), sh.k, scale, sh.Dv)
+    del inp
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    steps = max(1, min(args.steps, 5))
+    for _ in range(max(1, min(args.warmup, 2))):
+        pf.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        pf.index()
+        e[1].record(stream)
+        pf.topk()
+        e[2].record(stream)
+        pf.attend()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in ev])
+    t_idx, t_topk, t_mla = (float(x) for x in ms.mean(axis=0))
+    total = t_idx + t_topk + t_mla
+    n = np.arange(1, T + 1, dtype=np.float64)
+    idx_flops = float(n.sum()) * sh.HI * sh.dI * 2
+    kept = np.minimum(n, sh.k)
+    mla_flops = float(kept.sum()) * sh.H * (sh.Dqk + sh.Dv) * 2
+    idx_tf = idx_flops / (t_idx * 1e-3) / 1e12
+    mla_tf = mla_flops / (t_mla * 1e-3) / 1e12
+    out = {
+        "metric": "DSA prefill tokens/s at T=32768 (indexer+top-k+sparse MLA); % MFMA peak",
+        "value": T / (total * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "ms_per_step": total,
+        "higher_is_better": True,
+        "vs_baseline": None,
+        "dtype": "e4m3+bf16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "tokens": T, "top_k": sh.k, "heads": sh.H, "latent": sh.Dqk,
+                   "value_dim": sh.Dv, "indexer_heads": sh.HI, "indexer_dim": sh.dI},
+        "stages_ms": {"index": t_idx, "topk": t_topk, "sparse_mla": t_mla},
+        "roofline": {
+            "index": {"bound": "mfma", "achieved": idx_tf, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": idx_tf / FP8_PEAK_TFLOPS, "alg_flops": idx_flops},
+            "sparse_mla": {"bound": "mfma", "achieved": mla_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": mla_tf / BF16_PEAK_TFLOPS, "alg_flops": mla_flops},
+        },
     }
     print(json.dumps(out), flush=True)
 
