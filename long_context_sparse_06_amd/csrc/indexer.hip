@@ -19,6 +19,51 @@ namespace {
 constexpr int kIdxWaves = 8;
 constexpr int kIdxBatch = 64;  // keys per wave per loop trip: four 16-key MFMA column groups
 
+// Scores of one trip of 64 keys for 64 heads.  kb[u] holds lane (col, grp)'s 32 key bytes of
+// key 16*u + col (k-slice grp), qa[ht] the matching query bytes of heads 16*ht + col, wr the
+// weights of the heads the result layout leaves in this lane (16*ht + 4*grp + i).  Returns,
+// in lane l, the weighted ReLU head sum of key l of the trip (before the scales).
+__device__ __forceinline__ float trip_scores(const v8i (&qa)[4], const float (&wr)[4][4], const v8i (&kb)[4]) {
+  float part[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      // cbsz/blgp = 0: both operands OCP e4m3; scale exponent 127 = x1.
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb[u], acc, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum = fmaf(wr[ht][i], __builtin_amdgcn_fmed3f(acc[i], 0.0f, 3.0e38f), sum);
+    }
+    part[u] = sum;
+  }
+  // Stage 1 (lanes l, l^32): lower half keeps groups 0/1, upper half 2/3.
+  const v2i x02 = __builtin_amdgcn_permlane32_swap(__float_as_int(part[0]), __float_as_int(part[2]), false, false);
+  const v2i x13 = __builtin_amdgcn_permlane32_swap(__float_as_int(part[1]), __float_as_int(part[3]), false, false);
+  const float h02 = __int_as_float(x02[0]) + __int_as_float(x02[1]);
+  const float h13 = __int_as_float(x13[0]) + __int_as_float(x13[1]);
+  // Stage 2 (rows of 16 lanes, r and r^1): row g ends with group g's full sum.
+  const v2i y = __builtin_amdgcn_permlane16_swap(__float_as_int(h02), __float_as_int(h13), false, false);
+  return __int_as_float(y[0]) + __int_as_float(y[1]);
+}
+
+// Query fragments and head weights of one row in the lane layout trip_scores expects.
+__device__ __forceinline__ void load_query(const uint8_t* __restrict__ qr, const float* __restrict__ wrow,
+                                           int col, int grp, v8i (&qa)[4], float (&wr)[4][4]) {
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const uint4* p = reinterpret_cast<const uint4*>(qr + (16 * ht + col) * 128 + 32 * grp);
+    const uint4 a = p[0], b = p[1];
+    qa[ht] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  }
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const float4 v = *reinterpret_cast<const float4*>(wrow + 16 * ht + 4 * grp);
+    wr[ht][0] = v.x; wr[ht][1] = v.y; wr[ht][2] = v.z; wr[ht][3] = v.w;
+  }
+}
+
 // Score of 64 keys per loop trip and wave.  Lane (col, grp) feeds key s0 + 16*u + col, bytes
 // 32*grp .. 32*grp+31, to the MFMA of column group u; the result layout leaves the lane with
 // 16 of the 64 heads of that key, which are ReLU'd, weighted and summed in-lane.  A two-stage
@@ -54,22 +99,11 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     __syncthreads();
   }
 
-  // A operand: q[r, 16*ht + col, 32*grp .. 32*grp+31] (e4m3 bytes).
+  // A operand: q[r, 16*ht + col, 32*grp .. 32*grp+31] (e4m3 bytes); result rows held by
+  // this lane are heads 16*ht + 4*grp + i.
   v8i qa[4];
-  const uint8_t* qr = q + (int64_t)r * (64 * 128);
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const uint4* p = reinterpret_cast<const uint4*>(qr + (16 * ht + col) * 128 + 32 * grp);
-    const uint4 a = p[0], b = p[1];
-    qa[ht] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-  }
-  // Result rows held by this lane are heads 16*ht + 4*grp + i.
   float wr[4][4];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const float4 v = *reinterpret_cast<const float4*>(w + (int64_t)r * 64 + 16 * ht + 4 * grp);
-    wr[ht][0] = v.x; wr[ht][1] = v.y; wr[ht][2] = v.z; wr[ht][3] = v.w;
-  }
+  load_query(q + (int64_t)r * (64 * 128), w + (int64_t)r * 64, col, grp, qa, wr);
   const float qs = q_scale ? q_scale[r] : 1.0f;
   const int per_wave = keys_per_wg / kIdxWaves;
   const int64_t wbeg = wg_begin + (int64_t)wave * per_wave;
@@ -97,29 +131,190 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     }
     const int64_t s_out = s0 + lane;  // the key whose score this lane writes
     const float ks = kscale ? kscale[row_of(min(s_out, wend - 1))] : 1.0f;
-    float part[4];
+    const float tot = trip_scores(qa, wr, kb);
+    if (s_out < wend) srow[s_out] = tot * ks * qs;
+  }
+}
+
+// Many rows (prefill): one workgroup scores kRowsPerWg consecutive rows against one key range.
+// When the rows share a sequence (prefill rows do) a copy wave stages each 64-key trip once in
+// LDS with global_load_lds and every compute wave (one row each) reads it from there, so a key
+// crosses the vector-memory path once per workgroup instead of once per row; rows of
+// different sequences fall back to loading their own keys.  Trip layout: block 2*u + h
+// (1 KB) holds, at lane position col + 16*grp, bytes 32*grp + 16*h .. +15 of key 16*u + col --
+// the k-slice load_query gives the query operand -- so a 64-lane ds_read_b128 of a block is
+// one contiguous, conflict-free 1 KB; the 64 key scales follow.  Ring of three trips, two in flight; the slots are separate LDS variables and the
+// loop is unrolled by three so every slot is a compile-time variable (the copy wave never
+// reads the ring, the compute waves issue no copies).
+constexpr int kRowsPerWg = 8;
+constexpr int kRowsKernelMin = 512;  // calls with at least this many rows use the kernel below
+constexpr int kRowsThreads = (kRowsPerWg + 1) * WAVE;
+constexpr int kTripBytes = kIdxBatch * 128 + kIdxBatch * 4;
+constexpr int kKeyRing = 3;
+__shared__ __attribute__((aligned(16))) char g_kring0[kTripBytes];
+__shared__ __attribute__((aligned(16))) char g_kring1[kTripBytes];
+__shared__ __attribute__((aligned(16))) char g_kring2[kTripBytes];
+template <int S>
+__device__ __forceinline__ char* key_slot() {
+  return S == 0 ? g_kring0 : (S == 1 ? g_kring1 : g_kring2);
+}
+template <int S>
+struct KeySlot {
+  static constexpr int value = S;
+};
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(kRowsThreads) void index_fp8_rows_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ kdata, const float* __restrict__ kscale,
+    const int32_t* __restrict__ table, int max_pages, int page_size, int page_shift,
+    int64_t seq_stride, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
+    int R, float* __restrict__ scores, int64_t ld, int keys_per_wg) {
+  extern __shared__ int spage[];  // paged, shared rows: physical page of each logical page
+  const int r0 = blockIdx.x * kRowsPerWg;
+  const int nrows = min(kRowsPerWg, R - r0);
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
+  const int col = lane & 15, grp = lane >> 4;
+  // Every thread reads the workgroup's row list (uniform values).
+  int seq0 = row_seq[r0];
+  bool shared = true;
+  int64_t n_max = 0;
+  for (int i = 0; i < nrows; ++i) {
+    shared = shared && row_seq[r0 + i] == seq0;
+    n_max = max(n_max, (int64_t)row_pos[r0 + i] + 1);
+  }
+  const int64_t c0 = (int64_t)blockIdx.y * keys_per_wg;
+  if (c0 >= n_max) return;
+  const int64_t c1 = min(c0 + keys_per_wg, n_max);  // keys scored by this workgroup
+  const int my_r = r0 + min(wv, nrows - 1);
+  const bool my_valid = wv < nrows;
+  const int64_t my_n = my_valid ? (int64_t)row_pos[my_r] + 1 : 0;
+
+  auto row_in = [&](int seq, int64_t s, const int* pages, int64_t p_first) -> int64_t {
+    if (PAGED) {
+      const int64_t pg = page_shift >= 0 ? (s >> page_shift) : s / page_size;
+      const int64_t off = page_shift >= 0 ? (s & (page_size - 1)) : s % page_size;
+      const int phys = pages ? pages[pg - p_first] : table[(int64_t)seq * max_pages + pg];
+      return (int64_t)phys * page_size + off;
+    }
+    return (int64_t)seq * seq_stride + s;
+  };
+
+  if (!shared) {
+    // Rows of different sequences: wave wv scores its own row over [c0, min(c1, n_w)) with
+    // direct key loads.
+    if (wv >= kRowsPerWg || !my_valid) return;
+    const int seq = row_seq[my_r];
+    const int64_t end = min(c1, my_n);
+    if (c0 >= end) return;
+    v8i qa[4];
+    float wr[4][4];
+    load_query(q + (int64_t)my_r * (64 * 128), w + (int64_t)my_r * 64, col, grp, qa, wr);
+    const float qs = q_scale ? q_scale[my_r] : 1.0f;
+    float* srow = scores + (int64_t)my_r * ld;
+    for (int64_t s0 = c0; s0 < end; s0 += kIdxBatch) {
+      v8i kb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t row = row_in(seq, min(s0 + 16 * u + col, end - 1), nullptr, 0);
+        const uint4* p = reinterpret_cast<const uint4*>(kdata + row * 128 + 32 * grp);
+        const uint4 a = p[0], b = p[1];
+        kb[u] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+      }
+      const int64_t s_out = s0 + lane;
+      const float ks = kscale ? kscale[row_in(seq, min(s_out, end - 1), nullptr, 0)] : 1.0f;
+      const float tot = trip_scores(qa, wr, kb);
+      if (s_out < end) srow[s_out] = tot * ks * qs;
+    }
+    return;
+  }
+
+  // Shared sequence.  Paged: the workgroup's page-table slice goes to LDS first.
+  int64_t p_first = 0;
+  if (PAGED) {
+    p_first = page_shift >= 0 ? (c0 >> page_shift) : c0 / page_size;
+    const int64_t p_last = page_shift >= 0 ? ((c1 - 1) >> page_shift) : (c1 - 1) / page_size;
+    for (int i = tid; i <= (int)(p_last - p_first); i += kRowsThreads)
+      spage[i] = table[(int64_t)seq0 * max_pages + p_first + i];
+    __syncthreads();
+  }
+  const int ntrips = (int)((c1 - c0 + kIdxBatch - 1) / kIdxBatch);
+
+  if (wv == kRowsPerWg) {
+    // ---------------------------------------------------------------- copy wave
+    // Lane (col, grp) of block 2u + h fetches bytes 32*grp + 16*h of key 16u + col; lane l
+    // of the scale copy fetches key l's scale (4 bytes).
+    auto issue = [&](int t, char* dst) {
+      const int64_t s0 = c0 + (int64_t)t * kIdxBatch;
+      const uint32_t d = lds_offset(dst);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t row = row_in(seq0, min(s0 + 16 * u + col, c1 - 1), PAGED ? spage : nullptr, p_first);
+        const uint8_t* src = kdata + row * 128 + 32 * grp;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          __builtin_amdgcn_global_load_lds((const void*)(src + 16 * h), (lds_void*)(uintptr_t)(d + (2 * u + h) * 1024), 16, 0, 0);
+      }
+      if (kscale) {
+        const int64_t row = row_in(seq0, min(s0 + lane, c1 - 1), PAGED ? spage : nullptr, p_first);
+        __builtin_amdgcn_global_load_lds((const void*)(kscale + row), (lds_void*)(uintptr_t)(d + 8192), 4, 0, 0);
+      }
+    };
+    if (ntrips > 0) issue(0, key_slot<0>());
+    if (ntrips > 1) issue(1, key_slot<1>());
+    auto hand = [&](auto slot, int t) {
+      constexpr int S = decltype(slot)::value;
+      if (t + 1 < ntrips) {  // trip t landed, t+1 may be in flight
+        if (kscale) wait_vmcnt<9>(); else wait_vmcnt<8>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+      if (t + 2 < ntrips) issue(t + 2, key_slot<(S + 2) % kKeyRing>());
+    };
+    for (int t = 0; t < ntrips; t += kKeyRing) {
+      hand(KeySlot<0>{}, t);
+      if (t + 1 < ntrips) hand(KeySlot<1>{}, t + 1);
+      if (t + 2 < ntrips) hand(KeySlot<2>{}, t + 2);
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------------ compute waves
+  v8i qa[4];
+  float wr[4][4];
+  load_query(q + (int64_t)my_r * (64 * 128), w + (int64_t)my_r * 64, col, grp, qa, wr);
+  const float qs = (q_scale && my_valid) ? q_scale[my_r] : 1.0f;
+  const int64_t end = min(c1, my_n);
+  float* srow = scores + (int64_t)my_r * ld;
+  auto step = [&](auto slot, int t) {
+    constexpr int S = decltype(slot)::value;
+    __builtin_amdgcn_s_barrier();  // trip t is in slot S
+    const char* tb = key_slot<S>();
+    v8i kb[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        // cbsz/blgp = 0: both operands OCP e4m3; scale exponent 127 = x1.
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb[u], acc, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sum = fmaf(wr[ht][i], __builtin_amdgcn_fmed3f(acc[i], 0.0f, 3.0e38f), sum);
-      }
-      part[u] = sum;
+      const uint4 a = *reinterpret_cast<const uint4*>(tb + (2 * u) * 1024 + 16 * lane);
+      const uint4 b = *reinterpret_cast<const uint4*>(tb + (2 * u + 1) * 1024 + 16 * lane);
+      kb[u] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
     }
-    // Stage 1 (lanes l, l^32): lower half keeps groups 0/1, upper half 2/3.
-    const v2i x02 = __builtin_amdgcn_permlane32_swap(__float_as_int(part[0]), __float_as_int(part[2]), false, false);
-    const v2i x13 = __builtin_amdgcn_permlane32_swap(__float_as_int(part[1]), __float_as_int(part[3]), false, false);
-    const float h02 = __int_as_float(x02[0]) + __int_as_float(x02[1]);
-    const float h13 = __int_as_float(x13[0]) + __int_as_float(x13[1]);
-    // Stage 2 (rows of 16 lanes, r and r^1): row g ends with group g's full sum.
-    const v2i y = __builtin_amdgcn_permlane16_swap(__float_as_int(h02), __float_as_int(h13), false, false);
-    const float tot = __int_as_float(y[0]) + __int_as_float(y[1]);
-    if (s_out < wend) srow[s_out] = tot * ks * qs;
+    const float ks = kscale ? *reinterpret_cast<const float*>(tb + 8192 + 4 * lane) : 1.0f;
+    const float tot = trip_scores(qa, wr, kb);
+    const int64_t s_out = c0 + (int64_t)t * kIdxBatch + lane;
+    if (s_out < end) srow[s_out] = tot * ks * qs;
+  };
+  for (int t = 0; t < ntrips; t += kKeyRing) {
+    step(KeySlot<0>{}, t);
+    if (t + 1 < ntrips) step(KeySlot<1>{}, t + 1);
+    if (t + 2 < ntrips) step(KeySlot<2>{}, t + 2);
   }
 }
 
@@ -171,13 +366,31 @@ hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, cons
                                     const CacheView& keys, const int32_t* row_seq,
                                     const int32_t* row_pos, int R, int64_t n_bound, float* scores,
                                     int64_t ld, hipStream_t s) {
+  const uint8_t* kd = static_cast<const uint8_t*>(keys.data);
+  if (R >= kRowsKernelMin) {
+    // Many rows: eight rows per workgroup sharing staged key trips; 2048 keys per workgroup.
+    const int64_t kpw = 2048;
+    const dim3 grid((unsigned)((R + kRowsPerWg - 1) / kRowsPerWg), (unsigned)((n_bound + kpw - 1) / kpw));
+    if (keys.table) {
+      const int ps = keys.page_size;
+      const int shift = (ps & (ps - 1)) == 0 ? __builtin_ctz(ps) : -1;
+      const size_t lds = sizeof(int) * (size_t)(kpw / ps + 2);
+      index_fp8_rows_kernel<true><<<grid, kRowsThreads, lds, s>>>(
+          q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
+          R, scores, ld, (int)kpw);
+    } else {
+      index_fp8_rows_kernel<false><<<grid, kRowsThreads, 0, s>>>(
+          q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, R,
+          scores, ld, (int)kpw);
+    }
+    return hipGetLastError();
+  }
   // ~512 workgroups of 8 waves (two per CU at this kernel's register use); each wave's
   // share is a multiple of the 64-key trip.
   const int64_t total = (int64_t)R * n_bound;
   int64_t kpw = 512;
   while (kpw < 4096 && total / (kpw * 2) >= 512) kpw *= 2;
   const dim3 grid((unsigned)R, (unsigned)((n_bound + kpw - 1) / kpw));
-  const uint8_t* kd = static_cast<const uint8_t*>(keys.data);
   if (keys.table) {
     const int ps = keys.page_size;
     const int shift = (ps & (ps - 1)) == 0 ? __builtin_ctz(ps) : -1;

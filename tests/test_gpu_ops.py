@@ -57,6 +57,44 @@ def test_index_scores_fp8(paged):
         assert np.isnan(got[b, L:]).all(), "entries past n_valid must stay untouched"
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_index_scores_fp8_many_rows(paged):
+    """Calls with >= 512 rows take the eight-rows-per-workgroup kernel.  Groups of eight rows
+    that share a sequence (scattered positions, several key ranges, ragged tails) read staged
+    key trips; groups with mixed sequences load their own keys; the last group is partial."""
+    import long_context_sparse_06_amd as dsa
+    _case(f"index_scores_fp8 many rows paged={paged}")
+    lengths = np.array([4500, 300, 1300, 70])
+    inp = datagen.make_decode(4, None, FULL, seed=23, lengths=lengths, paged=paged)
+    d = upload_decode(inp)
+    R = 531
+    rng = np.random.default_rng(24)
+    qi = datagen.gaussian(rng, (R, FULL.HI, FULL.dI))
+    q_codes, q_scale = datagen.quantize_e4m3_per_token(qi.reshape(R, -1))
+    q_codes = q_codes.reshape(R, FULL.HI, FULL.dI)
+    w = rng.uniform(0.0, 1.0, size=(R, FULL.HI)).astype(np.float32)
+    seq = np.empty(R, dtype=np.int32)
+    for g in range(0, R, 8):
+        n = min(8, R - g)
+        seq[g:g + n] = (g // 8) % 4 if g < 320 else rng.integers(0, 4, size=n)
+    pos = np.array([rng.integers(0, lengths[s_]) for s_ in seq], dtype=np.int32)
+    pos[:8] = lengths[0] - 1 - np.arange(8)   # one group reaching the longest sequence's end
+    scores = torch.full((R, d.ld), float("nan"), device="cuda")
+    dsa.dsa_index_scores(dsa.E4M3, tensor(q_codes), tensor(q_scale), tensor(w),
+                         dsa.Cache(d.keys, d.k_scale, d.block_table, d.page_size, d.seq_stride),
+                         tensor(seq), tensor(pos), R, FULL.HI, FULL.dI, scores, d.ld)
+    got = scores.cpu().numpy()
+    keys = [pipeline.decode_keys(inp, b) for b in range(4)]
+    for r in range(R):
+        n = int(pos[r]) + 1
+        k_, ks = keys[seq[r]]
+        qd = decode_e4m3(q_codes[r])
+        ref = oracle.index_scores(qd, float(q_scale[r]), w[r], k_[:n], ks[:n])
+        ref_abs = parity.abs_scores(qd, float(q_scale[r]), w[r], k_[:n], ks[:n])
+        parity.check_scores(got[r, :n], ref, ref_abs, f"row {r} seq {seq[r]} pos {pos[r]}")
+        assert np.isnan(got[r, n:]).all(), f"row {r}: entries past its position must stay untouched"
+
+
 def test_index_scores_fp8_negative_weights_and_zero_query():
     import long_context_sparse_06_amd as dsa
     _case("index_scores_fp8 signs")
