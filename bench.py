@@ -129,6 +129,20 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # ---- per-step spread: HIP events around single replays (outside the wall-clock loop)
+    spread = None
+    if use_graph:
+        n_ev = min(args.steps, 100)
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+        for i, (a, b) in enumerate(sev):
+            a.record(stream)
+            one(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) for a, b in sev]) * 1e3
+        spread = {"p10": float(np.percentile(per, 10)), "p50": float(np.median(per)),
+                  "p90": float(np.percentile(per, 90)), "n": n_ev}
+
     # ---- eager pass with HIP events around each op (on the stream the kernels run on)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(min(args.warmup, 5)):
@@ -160,6 +174,33 @@ def main():
         graphs[0].replay()
         torch.cuda.synchronize()
         ok = torch.equal(ref[0], steps[0].idx) and torch.equal(ref[1].view(torch.int16), steps[0].out.view(torch.int16))
+
+    # ---- top-k on a tie storm (every score equal) beside the same call on the step's scores
+    st0 = steps[0]
+    storm = torch.full_like(st0.scores, 0.5)
+    tie = {}
+    for name, buf in (("step_scores", st0.scores), ("tie_storm", storm)):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a, b in evs:
+            a.record(stream)
+            dsa.dsa_topk(buf, st0.ld, st0.n_valid, st0.B, st0.k, st0.idx, st0.topk_ws, st0.topk_ws_bytes, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        tie[name + "_us"] = float(np.mean([a.elapsed_time(b) for a, b in evs[2:]]) * 1e3)
+    del storm
+
+    # ---- achievable HBM bandwidth on this GPU: a 1 GiB device-to-device copy (read + write)
+    src_b = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst_b = torch.empty_like(src_b)
+    dst_b.copy_(src_b)
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca.record(stream)
+    for _ in range(5):
+        dst_b.copy_(src_b)
+    cb.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (1 << 30) / (ca.elapsed_time(cb) * 1e6)
+    del src_b, dst_b
 
     # ---- CPU oracle on this host (bounded sample of the same workload)
     cpu = None
@@ -219,7 +260,12 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "alg_bytes_per_launch": idx_bytes},
         "step_roofline": {"alg_bytes": step_bytes, "roof_us": roof_us,
-                          "frac": roof_us / (ms_per_step * 1e3)},
+                          "frac": roof_us / (ms_per_step * 1e3),
+                          "achievable_copy_GBs": copy_gbs,
+                          "frac_of_achievable": step_bytes / (copy_gbs * 1e3) / (ms_per_step * 1e3),
+                          "index_frac_of_achievable": achieved / copy_gbs},
+        "step_us_spread": spread,
+        "topk_diagnostic": tie,
         "breakdown_us": {"index": idx_us, "topk": float(t_topk.mean()), "sparse_mla": float(t_mla.mean()),
                          "eager_step": (te1 - te0) * 1e6 / args.steps},
         "graph_replay_matches_eager": bool(ok),

@@ -105,7 +105,8 @@ dsa_status dsa_index_scores(dsa_dtype dt, const void* q, const float* q_scale, c
  *   scores [R, ld] fp32      n_valid [R] int32, 0 <= n_valid[r] <= ld
  *   idx    [R, k] int32 output
  *   ws     device workspace of at least dsa_topk_workspace_size(R, ld, k) bytes
- * Limits: k <= 16384, ld <= 2^24.
+ * Limits: k <= 16384, ld <= 2^24, and for ld > 32768 R * ceil(ld / 4096) <= 2^31 - 1
+ * (DSA_ERR_SHAPE otherwise).
  */
 size_t dsa_topk_workspace_size(int R, int64_t ld, int k);
 dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,

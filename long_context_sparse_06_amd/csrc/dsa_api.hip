@@ -63,7 +63,8 @@ size_t dsa_topk_workspace_size(int R, int64_t ld, int k) {
 dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
                     int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!scores || !n_valid || !idx) return DSA_ERR_NULL;
-  if (R <= 0 || k <= 0 || ld <= 0 || k > 16384 || ld > (int64_t(1) << 24) || R > 2147483647 / 2)
+  if (R <= 0 || k <= 0 || ld <= 0 || k > 16384 || ld > (int64_t(1) << 24) || R > 2147483647 / 2 ||
+      !dsa::topk_shape_ok(R, ld))
     return DSA_ERR_SHAPE;
   const size_t need = dsa::topk_workspace_bytes(R, ld, k);
   if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;

@@ -76,11 +76,14 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     const uint8_t* __restrict__ kdata, const float* __restrict__ kscale,
     const int32_t* __restrict__ table, int max_pages, int page_size, int page_shift,
     int64_t seq_stride, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
-    float* __restrict__ scores, int64_t ld, int keys_per_wg) {
+    float* __restrict__ scores, int64_t ld, int keys_per_wg, int n_chunks) {
   extern __shared__ int spage[];  // paged: physical page of each logical page of this range
-  const int r = blockIdx.x;
+  // Block b takes chunk b % n_chunks of row b / n_chunks: consecutive blocks (which the
+  // dispatcher deals round-robin to the eight XCDs) walk along a row, so rows of different
+  // lengths still spread their work evenly over the XCDs.
+  const int r = blockIdx.x / n_chunks;
   const int64_t n = (int64_t)row_pos[r] + 1;
-  const int64_t wg_begin = (int64_t)blockIdx.y * keys_per_wg;
+  const int64_t wg_begin = (int64_t)(blockIdx.x % n_chunks) * keys_per_wg;
   if (wg_begin >= n) return;
   const int64_t wg_end = min(wg_begin + keys_per_wg, n);
   const int tid = threadIdx.x;
@@ -390,18 +393,19 @@ hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, cons
   const int64_t total = (int64_t)R * n_bound;
   int64_t kpw = 512;
   while (kpw < 4096 && total / (kpw * 2) >= 512) kpw *= 2;
-  const dim3 grid((unsigned)R, (unsigned)((n_bound + kpw - 1) / kpw));
+  const int n_chunks = (int)((n_bound + kpw - 1) / kpw);
+  const unsigned grid = (unsigned)R * (unsigned)n_chunks;
   if (keys.table) {
     const int ps = keys.page_size;
     const int shift = (ps & (ps - 1)) == 0 ? __builtin_ctz(ps) : -1;
     const size_t lds = sizeof(int) * (size_t)(kpw / ps + 2);
     index_fp8_kernel<true><<<grid, kIdxWaves * WAVE, lds, s>>>(
         q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
-        scores, ld, (int)kpw);
+        scores, ld, (int)kpw, n_chunks);
   } else {
     index_fp8_kernel<false><<<grid, kIdxWaves * WAVE, 0, s>>>(
         q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, scores,
-        ld, (int)kpw);
+        ld, (int)kpw, n_chunks);
   }
   return hipGetLastError();
 }

@@ -27,6 +27,8 @@ hipError_t launch_index_generic(bool fp8, const void* q, const float* q_scale, c
 
 // ---- top-k
 size_t topk_workspace_bytes(int R, int64_t ld, int k);
+// False when R rows of length ld need more blocks than one launch can take.
+bool topk_shape_ok(int R, int64_t ld);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
                        int32_t* idx, void* ws, hipStream_t s);
 

@@ -379,56 +379,63 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   }
 }
 
-// Log-sum-exp merge of the split partials: 128 threads per (row, head), 4 value columns
-// per thread.  Split s contributes its normalized output u_s with weight l_s * 2^(m_s - M).
-// Splits are taken 16 at a time with every load of a batch (values and the (max, sum) pairs
-// alike) issued before any is used, so a typical merge is one round trip; batches after the
-// first rescale the running sums to the new maximum.
-constexpr int kCombineBatch = 16;
+// Log-sum-exp merge of the split partials: one wave per (row, head), 8 value columns per
+// lane (16-byte loads and stores).  Split s contributes its normalized output u_s with
+// weight l_s * 2^(m_s - M).  Splits are taken NB at a time (NB = the split count rounded up
+// to a power of two, at most 16) with every load of a batch -- values and the (max, sum)
+// pairs alike -- issued before any is used, so a typical merge is one round trip; batches
+// after the first rescale the running sums to the new maximum.
+constexpr int kCombinePairs = 4;  // (row, head) pairs per 256-thread workgroup
+template <int NB>
 __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int RH, int H, int n_split,
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
-  const int pair = blockIdx.x * 2 + threadIdx.x / 128;
+  const int pair = blockIdx.x * kCombinePairs + threadIdx.x / WAVE;
   if (pair >= RH) return;
   const int r = pair / H, h = pair % H;
-  const int t = threadIdx.x & 127;
+  const int t = threadIdx.x & (WAVE - 1);
   const int64_t p0 = (int64_t)r * n_split * H + h;  // partial of split s at p0 + s * H
   float M = -INFINITY, L = 0.0f;
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
-    float2 ml[kCombineBatch];
-    uint2 v[kCombineBatch];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_split; s0 += NB) {
+    float2 ml[NB];
+    uint4 v[NB];
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) {
+    for (int u = 0; u < NB; ++u) {
       const int64_t pr = p0 + (int64_t)min(s0 + u, n_split - 1) * H;
       ml[u] = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
-      v[u] = *reinterpret_cast<const uint2*>(part_o + pr * kDv + 4 * t);
+      v[u] = *reinterpret_cast<const uint4*>(part_o + pr * kDv + 8 * t);
     }
     float Mb = M;
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u)
+    for (int u = 0; u < NB; ++u)
       if (s0 + u < n_split && ml[u].y > 0.0f) Mb = fmaxf(Mb, ml[u].x);
     const float c = M == -INFINITY ? 0.0f : exp2f(M - Mb);
     L *= c;
-    acc.x *= c; acc.y *= c; acc.z *= c; acc.w *= c;
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) {
+    for (int j = 0; j < 8; ++j) acc[j] *= c;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
       const bool valid = s0 + u < n_split && ml[u].y > 0.0f;
       const float f = valid ? ml[u].y * exp2f(ml[u].x - Mb) : 0.0f;
       L += f;
-      acc.x += __uint_as_float(v[u].x << 16) * f;
-      acc.y += __uint_as_float(v[u].x & 0xFFFF0000u) * f;
-      acc.z += __uint_as_float(v[u].y << 16) * f;
-      acc.w += __uint_as_float(v[u].y & 0xFFFF0000u) * f;
+      const uint32_t wv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += __uint_as_float(wv[j] << 16) * f;
+        acc[2 * j + 1] += __uint_as_float(wv[j] & 0xFFFF0000u) * f;
+      }
     }
     M = Mb;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  const uint32_t lo = f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
-  const uint32_t hi = f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
-  *reinterpret_cast<uint2*>(out + ((int64_t)r * H + h) * kDv + 4 * t) = make_uint2(lo, hi);
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = f32_to_bf16(acc[2 * j] * inv) | ((uint32_t)f32_to_bf16(acc[2 * j + 1] * inv) << 16);
+  *reinterpret_cast<uint4*>(out + ((int64_t)r * H + h) * kDv + 8 * t) = make_uint4(o[0], o[1], o[2], o[3]);
   if (lse && t == 0) lse[(int64_t)r * H + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
@@ -555,7 +562,15 @@ hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split <= 1) return e;
   const int RH = R * H;
-  mla_combine_kernel<<<(RH + 1) / 2, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
+  const unsigned cgrid = (unsigned)((RH + kCombinePairs - 1) / kCombinePairs);
+  if (p.n_split <= 2)
+    mla_combine_kernel<2><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
+  else if (p.n_split <= 4)
+    mla_combine_kernel<4><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
+  else if (p.n_split <= 8)
+    mla_combine_kernel<8><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
+  else
+    mla_combine_kernel<16><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
   return hipGetLastError();
 }
 

@@ -15,7 +15,8 @@
 // ballots, so the elements equal to T are taken lowest index first and the output comes
 // out sorted.
 //
-// Rows up to kRowMax scores are selected by one workgroup entirely in LDS.  Longer rows
+// Rows up to kRowMax scores are selected by one workgroup that holds the row in registers
+// (read from memory once) and keeps only the histograms in LDS.  Longer rows
 // (decode at 128k context) take three launches: one workgroup per row draws an evenly
 // spaced sample and sets a threshold theta whose expected survivor count is ~2k; many
 // workgroups per row compact the survivors (in index order); one workgroup per row then
@@ -32,7 +33,7 @@
 namespace dsa {
 namespace {
 
-constexpr int kRowMax = 32768;     // longest row selected wholly in LDS (128 KiB of keys)
+constexpr int kRowMax = 32768;     // longest row selected by one workgroup (32 keys per thread)
 constexpr int kSample = 2048;      // sample size for longer rows
 constexpr int kChunk = 4096;       // scores per workgroup in the long-row compaction pass
 constexpr int kCandCap = 12288;    // survivors resolvable in LDS (96 KiB of key/index pairs)
@@ -199,28 +200,16 @@ __device__ __forceinline__ void publish_range(uint32_t lmn, uint32_t lmx, int* h
 // range, typically while it loaded the keys, which saves a pass and a barrier.  `slack`
 // lets the search stop early, with `exact` set, once the bin holds at most `slack` more
 // elements than needed -- only for callers content with up to k + slack elements >= T.
-template <int NT, bool RANGED = false, class Src>
-__device__ Threshold find_threshold(const Src& src, int m, int k, int* hist, SelState& st,
-                                    int slack = 0) {
+// The digit passes of find_threshold on the key interval [lo, hi]; fill(lo, hi, s, h) adds
+// every element whose key lies in [lo, hi] to bin (key - lo) >> s of h.
+template <int NT, class Fill>
+__device__ Threshold radix_threshold(uint32_t lo, uint32_t hi, int k, int* hist, SelState& st, int slack,
+                                     Fill&& fill) {
   constexpr int NW = NT / WAVE;
   constexpr int PER = kHistBins / NT;
   static_assert(PER * NT == kHistBins, "bins per thread");
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  if (!RANGED) {
-    uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
-    for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
-      lmn = min(lmn, key);
-      lmx = max(lmx, key);
-    });
-    publish_range<NT>(lmn, lmx, hist, st);
-    __syncthreads();
-  }
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    lo = min(lo, st.wmin[i]);
-    hi = max(hi, st.wmax[i]);
-  }
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int w = tid / WAVE;
   const uint32_t top = hi;
   int need = k;
   bool exact = false;
@@ -229,9 +218,7 @@ __device__ Threshold find_threshold(const Src& src, int m, int k, int* hist, Sel
     const int s = max(0, 32 - __builtin_clz(width) - 11);
     const int nb = (int)(width >> s) + 1;
     int* h = hist + pass * kHistBins;
-    for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
-      if (key >= lo && key <= hi) atomicAdd(&h[(key - lo) >> s], 1);
-    });
+    fill(lo, hi, s, h);
     __syncthreads();
     // Thread t owns bins nb-1-PER*t-j (j < PER): bins counted from the top.
     int cb[PER];
@@ -277,6 +264,45 @@ __device__ Threshold find_threshold(const Src& src, int m, int k, int* hist, Sel
     }
   }
   return Threshold{lo, need, exact, top};
+}
+
+// Finds the selection threshold of the top-k (1 <= k <= m) among m elements with
+// range-relative radix digits: the threshold lies in the key interval [lo, hi]; each pass
+// splits it into at most 2048 equal bins of 2^s keys (s chosen from its width), so the
+// histogram resolves wherever the keys actually are, in at most three passes.  Each pass
+// has two barriers: after the histogram, and after the per-wave totals; every wave then
+// finds the crossing wave from the totals and rescans that wave's bins itself, so the
+// result needs no broadcast.  Each pass has its own histogram buffer (cleared up front),
+// so no clearing races a slower wave's rescan.  All NT threads must call it.
+//
+// RANGED: the caller has already run publish_range (and a barrier) with every thread's key
+// range, typically while it loaded the keys, which saves a pass and a barrier.  `slack`
+// lets the search stop early, with `exact` set, once the bin holds at most `slack` more
+// elements than needed -- only for callers content with up to k + slack elements >= T.
+template <int NT, bool RANGED = false, class Src>
+__device__ Threshold find_threshold(const Src& src, int m, int k, int* hist, SelState& st,
+                                    int slack = 0) {
+  constexpr int NW = NT / WAVE;
+  if (!RANGED) {
+    uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
+    for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
+      lmn = min(lmn, key);
+      lmx = max(lmx, key);
+    });
+    publish_range<NT>(lmn, lmx, hist, st);
+    __syncthreads();
+  }
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    lo = min(lo, st.wmin[i]);
+    hi = max(hi, st.wmax[i]);
+  }
+  return radix_threshold<NT>(lo, hi, k, hist, st, slack, [&](uint32_t a, uint32_t b, int s, int* h) {
+    for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
+      if (key >= a && key <= b) atomicAdd(&h[(key - a) >> s], 1);
+    });
+  });
 }
 
 // Writes the ids of the selected elements, in ascending position order, to out[0..k).
@@ -361,8 +387,11 @@ __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
   __shared__ __attribute__((aligned(16))) int hist[kPassMax * kHistBins];
   __shared__ SelState st;
   constexpr int NW = kLongThreads / WAVE;
-  const int r = blockIdx.x;
-  const int c = blockIdx.y;
+  // Block b takes chunk b % max_chunks of row b / max_chunks, so consecutive blocks (dealt
+  // round-robin to the eight XCDs) walk along a row and rows of different lengths spread
+  // evenly over the XCDs.
+  const int r = blockIdx.x / max_chunks;
+  const int c = blockIdx.x % max_chunks;
   int64_t n64 = n_valid[r];
   n64 = n64 < 0 ? 0 : (n64 > ld ? ld : n64);
   const int n = (int)n64;
@@ -449,6 +478,170 @@ __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
   if (tid == kLongThreads - 1) counts[(int64_t)r * max_chunks + c] = (uint32_t)off;
 }
 
+// Exact top-k among `total` survivors (keys/ids in LDS, in index order) that all lie at or
+// above theta and have been histogrammed into kSurvBins bins of 2^shift keys above theta
+// (the last bin open-ended).  One block scan finds the bin b* holding the k-th largest;
+// its keys are then ranked directly, or by the radix select when there are too many.  The
+// caller has passed a barrier since the histogram was complete and has cleared st.ntie.
+__device__ __forceinline__ void select_survivors(const uint32_t* keys, const int* ids, int total, uint32_t theta,
+                                 uint32_t shift, int k, int* hist, uint2* ties, SelState& st,
+                                 int32_t* __restrict__ out) {
+  constexpr int NW = kResolveThreads / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  // Bin b* of the k-th largest survivor: thread t holds bins 4095-4t .. 4092-4t (top down);
+  // every wave then finds the crossing wave from the per-wave totals and rescans its bins.
+  const int4 hv = reinterpret_cast<const int4*>(hist)[kResolveThreads - 1 - tid];
+  const int incl = wave_incl_scan(hv.x + hv.y + hv.z + hv.w);
+  if (lane == WAVE - 1) st.wscan[w] = incl;
+  __syncthreads();
+  int before = 0, vc = -1;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const int tv = st.wscan[v];
+    const bool hit = vc < 0 && before + tv >= k;
+    before += (vc < 0 && !hit) ? tv : 0;
+    vc = hit ? v : vc;
+  }
+  const int4 hc = reinterpret_cast<const int4*>(hist)[kResolveThreads - 1 - (vc * WAVE + lane)];
+  const int cb[4] = {hc.w, hc.z, hc.y, hc.x};
+  int bstar, above, bcnt;
+  wave_crossing<4>(cb, kSurvBins - 1 - 4 * (vc * WAVE + lane), before, k, bstar, above, bcnt);
+  const int need = k - above;
+  const uint32_t t_lo = theta + ((uint32_t)bstar << shift);  // first key of bin b*
+  const LdsPairs src{keys, ids};
+  Threshold th;
+  if (bcnt == need) {
+    th = Threshold{t_lo, 0, true, 0u};  // all of bin b* and above: { key >= t_lo }
+  } else if (bcnt <= kTieMax) {
+    // Rank the keys of bin b* by (key descending, position ascending); the one of rank
+    // need-1 is the threshold T, and need - (keys of the bin above T) of those equal to T
+    // are taken, lowest position first -- the same rule the emit pass applies.
+    const uint64_t bin_end = (uint64_t)t_lo + ((uint64_t)1 << shift) - 1;  // may pass 2^32
+    const uint32_t t_hi = (bstar == kSurvBins - 1 || bin_end > 0xFFFFFFFFull) ? 0xFFFFFFFFu : (uint32_t)bin_end;
+    for (int i0 = 0; i0 < total; i0 += kResolveThreads * 4) {
+      uint32_t kv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kv[u] = keys[min(i0 + u * kResolveThreads + tid, total - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kResolveThreads + tid;
+        const bool in = (i < total) & (kv[u] >= t_lo) & (kv[u] <= t_hi);
+        const uint64_t im = ballot(in);
+        if (im) {  // one slot reservation per wave and round
+          int slot = 0;
+          if (lane == 0) slot = atomicAdd(&st.ntie, __popcll(im));
+          slot = readlane(slot, 0);
+          if (in) ties[slot + mask_rank(im)] = make_uint2(kv[u], (uint32_t)i);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < bcnt) {
+      const uint2 me = ties[tid];
+      int gt = 0, eq_before = 0;
+      for (int j = 0; j < bcnt; ++j) {
+        const uint2 o = ties[j];
+        gt += o.x > me.x;
+        eq_before += (o.x == me.x) & (o.y < me.y);
+      }
+      if (gt + eq_before == need - 1) {
+        st.tie_T = me.x;
+        st.tie_need = need - gt;
+      }
+    }
+    __syncthreads();
+    th = Threshold{st.tie_T, st.tie_need, false, 0u};
+  } else {
+    __syncthreads();  // every wave has read the survivor histogram before the radix select clears it
+    th = find_threshold<kResolveThreads>(src, total, k, hist, st);
+  }
+  emit_selected<kResolveThreads>(src, total, th, st, out);
+}
+
+// Rows of at most kRowMax scores (one workgroup each): the radix select and the emit pass
+// above with the row held in registers -- wave w holds the contiguous index range
+// [w*per, w*per + per) in rounds of 64, KPT keys per thread -- so the row is read from
+// memory once and only the histograms live in LDS.  The loads are unconditional (clamped
+// to the last element) so they all issue back to back; a branch around each would make the
+// compiler wait for each in turn.
+template <int KPT>
+__device__ void select_mid_row(const float* __restrict__ row, int n, int k, int32_t* __restrict__ out,
+                               int* hist, SelState& st) {
+  constexpr int NT = kRowThreads, NW = NT / WAVE;
+  static_assert(KPT * NT <= kRowMax, "keys per thread");
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int per = ((n + NW - 1) / NW + WAVE - 1) / WAVE * WAVE;  // <= KPT * WAVE
+  const int beg = w * per;
+  const int end = min(n, beg + per);
+  // Positions past the wave's range get key 0, below every non-NaN score's key (the key of
+  // -inf is 0x007FFFFF), so no later pass needs a range test: they never reach a histogram
+  // range or the threshold.
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = float_key(row[min(beg + j * WAVE + lane, n - 1)]);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = beg + j * WAVE + lane < end ? key[j] : 0u;
+  uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    lmn = min(lmn, key[j] ? key[j] : 0xFFFFFFFFu);
+    lmx = max(lmx, key[j]);
+  }
+  publish_range<NT>(lmn, lmx, hist, st);
+  __syncthreads();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    lo = min(lo, st.wmin[i]);
+    hi = max(hi, st.wmax[i]);
+  }
+  const Threshold th = radix_threshold<NT>(lo, hi, k, hist, st, 0, [&](uint32_t a, uint32_t b, int s, int* h) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if ((key[j] >= a) & (key[j] <= b)) atomicAdd(&h[(key[j] - a) >> s], 1);
+  });
+  // Emit: per-wave counts of keys above T and equal to T, then the waves' offsets from two
+  // DPP scans (ties taken in wave order, lowest index first), then the ballot-ranked writes.
+  const uint32_t T = th.T;
+  const bool ex = th.exact;
+  const int need = ex ? 0 : th.need;
+  int cgt = 0, ceq = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    cgt += __popcll(ballot((key[j] > T) | (ex & (key[j] == T))));
+    ceq += __popcll(ballot(!ex & (key[j] == T)));
+  }
+  if (lane == 0) {
+    st.wtot[0][w] = cgt;
+    st.wtot[1][w] = ceq;
+    st.wred[w] = T;
+  }
+  __syncthreads();
+  // T comes back through LDS so the compiler recomputes the comparisons below instead of
+  // keeping the count pass's 2 x KPT lane masks alive (in spilled scalar registers).
+  const uint32_t T2 = st.wred[w];
+  const int gt_v = lane < NW ? st.wtot[0][lane] : 0;
+  const int eq_v = lane < NW ? st.wtot[1][lane] : 0;
+  const int eq_before_v = wave_incl_scan(eq_v) - eq_v;
+  const int take_v = min(max(need - eq_before_v, 0), eq_v);
+  const int sel_v = gt_v + take_v;
+  const int sel_before_v = wave_incl_scan(sel_v) - sel_v;
+  const int eq_before = readlane(eq_before_v, w);
+  int sel_run = readlane(sel_before_v, w);
+  int eq_run = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool gt = (key[j] > T2) | (ex & (key[j] == T2));
+    const bool eq = !ex & (key[j] == T2);
+    const uint64_t eqm = ballot(eq);
+    const bool sel = gt | (eq & (eq_before + eq_run + mask_rank(eqm) < need));
+    const uint64_t selm = ballot(sel);
+    if (sel) out[sel_run + mask_rank(selm)] = beg + j * WAVE + lane;
+    eq_run += __popcll(eqm);
+    sel_run += __popcll(selm);
+  }
+}
+
 // Long rows, pass 2 (one workgroup per row): exact top-k among the survivors in LDS, or
 // among the whole row when the sample threshold kept fewer than k or more than fit.  The
 // survivors are histogrammed into kSurvBins bins above theta as they are gathered, so the
@@ -514,74 +707,7 @@ __device__ void resolve_long_row(const float* __restrict__ row, int ld, int n, i
     }
   }
   __syncthreads();
-  // Bin b* of the k-th largest survivor: thread t holds bins 4095-4t .. 4092-4t (top down);
-  // every wave then finds the crossing wave from the per-wave totals and rescans its bins.
-  const int4 hv = reinterpret_cast<const int4*>(hist)[kResolveThreads - 1 - tid];
-  const int incl = wave_incl_scan(hv.x + hv.y + hv.z + hv.w);
-  if (lane == WAVE - 1) st.wscan[w] = incl;
-  __syncthreads();
-  int before = 0, vc = -1;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    const int tv = st.wscan[v];
-    const bool hit = vc < 0 && before + tv >= k;
-    before += (vc < 0 && !hit) ? tv : 0;
-    vc = hit ? v : vc;
-  }
-  const int4 hc = reinterpret_cast<const int4*>(hist)[kResolveThreads - 1 - (vc * WAVE + lane)];
-  const int cb[4] = {hc.w, hc.z, hc.y, hc.x};
-  int bstar, above, bcnt;
-  wave_crossing<4>(cb, kSurvBins - 1 - 4 * (vc * WAVE + lane), before, k, bstar, above, bcnt);
-  const int need = k - above;
-  const uint32_t t_lo = rh.theta + ((uint32_t)bstar << rh.shift);  // first key of bin b*
-  const LdsPairs src{keys, ids};
-  Threshold th;
-  if (bcnt == need) {
-    th = Threshold{t_lo, 0, true, 0u};  // all of bin b* and above: { key >= t_lo }
-  } else if (bcnt <= kTieMax) {
-    // Rank the keys of bin b* by (key descending, position ascending); the one of rank
-    // need-1 is the threshold T, and need - (keys of the bin above T) of those equal to T
-    // are taken, lowest position first -- the same rule the emit pass applies.
-    const uint64_t bin_end = (uint64_t)t_lo + ((uint64_t)1 << rh.shift) - 1;  // may pass 2^32
-    const uint32_t t_hi = (bstar == kSurvBins - 1 || bin_end > 0xFFFFFFFFull) ? 0xFFFFFFFFu : (uint32_t)bin_end;
-    for (int i0 = 0; i0 < total; i0 += kResolveThreads * 4) {
-      uint32_t kv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kv[u] = keys[min(i0 + u * kResolveThreads + tid, total - 1)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kResolveThreads + tid;
-        const bool in = (i < total) & (kv[u] >= t_lo) & (kv[u] <= t_hi);
-        const uint64_t im = ballot(in);
-        if (im) {  // one slot reservation per wave and round
-          int slot = 0;
-          if (lane == 0) slot = atomicAdd(&st.ntie, __popcll(im));
-          slot = readlane(slot, 0);
-          if (in) ties[slot + mask_rank(im)] = make_uint2(kv[u], (uint32_t)i);
-        }
-      }
-    }
-    __syncthreads();
-    if (tid < bcnt) {
-      const uint2 me = ties[tid];
-      int gt = 0, eq_before = 0;
-      for (int j = 0; j < bcnt; ++j) {
-        const uint2 o = ties[j];
-        gt += o.x > me.x;
-        eq_before += (o.x == me.x) & (o.y < me.y);
-      }
-      if (gt + eq_before == need - 1) {
-        st.tie_T = me.x;
-        st.tie_need = need - gt;
-      }
-    }
-    __syncthreads();
-    th = Threshold{st.tie_T, st.tie_need, false, 0u};
-  } else {
-    __syncthreads();  // every wave has read the survivor histogram before the radix select clears it
-    th = find_threshold<kResolveThreads>(src, total, k, hist, st);
-  }
-  emit_selected<kResolveThreads>(src, total, th, st, out);
+  select_survivors(keys, ids, total, rh.theta, rh.shift, k, hist, ties, st, out);
 }
 
 // One workgroup per row: trivial rows, LDS-resident rows, or the resolve of long rows.
@@ -590,7 +716,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     int32_t* __restrict__ idx, const RowHeader* __restrict__ hdr, const uint32_t* __restrict__ counts,
     int max_chunks, const uint2* __restrict__ cand) {
   static_assert(kRowThreads == kResolveThreads, "one kernel serves both paths");
-  extern __shared__ uint32_t smem[];  // row keys, or survivor keys, ids and chunk offsets
+  extern __shared__ uint32_t smem[];  // long rows: survivor keys, ids and chunk offsets
   __shared__ __attribute__((aligned(16))) int hist[kPassMax * kHistBins];
   __shared__ uint2 ties[kTieMax];
   __shared__ SelState st;
@@ -605,17 +731,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     return;
   }
   if (n <= kRowMax) {
-    uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
-    for_each_key<kRowThreads, 16>(GlobalRow{row}, n, [&](int i, uint32_t key) {
-      smem[i] = key;
-      lmn = min(lmn, key);
-      lmx = max(lmx, key);
-    });
-    publish_range<kRowThreads>(lmn, lmx, hist, st);
-    __syncthreads();
-    const LdsKeys src{smem, 0};
-    const Threshold th = find_threshold<kRowThreads, true>(src, n, k, hist, st);
-    emit_selected<kRowThreads>(src, n, th, st, out);
+    if (n <= kRowMax / 4) select_mid_row<kRowMax / 4 / kRowThreads>(row, n, k, out, hist, st);
+    else if (n <= kRowMax / 2) select_mid_row<kRowMax / 2 / kRowThreads>(row, n, k, out, hist, st);
+    else select_mid_row<kRowMax / kRowThreads>(row, n, k, out, hist, st);
     return;
   }
   resolve_long_row(row, (int)ld, n, k, r, out, hdr, counts, max_chunks, cand, smem, hist, ties, st);
@@ -640,6 +758,10 @@ WsLayout ws_layout(int R, int64_t ld) {
 
 }  // namespace
 
+bool topk_shape_ok(int R, int64_t ld) {
+  return (int64_t)R * ws_layout(1, ld).max_chunks <= 2147483647LL;
+}
+
 size_t topk_workspace_bytes(int R, int64_t ld, int k) {
   (void)k;
   return ws_layout(R, ld).total;
@@ -653,14 +775,14 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, 
   uint32_t* counts = L.total ? reinterpret_cast<uint32_t*>(wsb + L.counts) : nullptr;
   uint2* cand = L.total ? reinterpret_cast<uint2*>(wsb + L.cand) : nullptr;
   if (L.total) {
-    topk_prep_kernel<<<dim3(R, L.max_chunks), kLongThreads, 0, s>>>(scores, ld, n_valid, k, hdr, counts,
-                                                                  L.max_chunks, cand);
+    topk_prep_kernel<<<(unsigned)R * (unsigned)L.max_chunks, kLongThreads, 0, s>>>(
+        scores, ld, n_valid, k, hdr, counts, L.max_chunks, cand);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t row_lds = sizeof(uint32_t) * (size_t)(ld < kRowMax ? ld : kRowMax);
-  const size_t long_lds = L.total ? sizeof(uint32_t) * (2 * (size_t)kCandCap + L.max_chunks + 1) : 0;
-  topk_finish_kernel<<<R, kRowThreads, row_lds > long_lds ? row_lds : long_lds, s>>>(
+  // Long rows: survivor keys and ids, then the chunk offsets (rows up to kRowMax need none).
+  const size_t lds = L.total ? sizeof(uint32_t) * (2 * (size_t)kCandCap + L.max_chunks + 1) : 0;
+  topk_finish_kernel<<<R, kRowThreads, lds, s>>>(
       scores, ld, n_valid, k, idx, hdr, counts, L.max_chunks, cand);
   return hipGetLastError();
 }

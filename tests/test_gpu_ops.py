@@ -179,6 +179,27 @@ def test_topk_lds_row_max_and_small_k():
         _expect_topk(s, [32768, 32768, 20000], k, got)
 
 
+def test_topk_mid_rows_sampled_and_fallback():
+    """Rows of 12289..32768 scores take a sample threshold before compaction; all-equal and
+    coarse rows overflow the survivor list and fall back to the full row; a row whose largest
+    scores sit on half the sampled positions keeps fewer than k survivors and falls back too."""
+    _case("topk mid rows")
+    rng = np.random.default_rng(35)
+    ld, k = 32768, 2048
+    n_valid = [32768, 12289, 20000, 32768, 30000, 32768, 16000, 12288, 25000]
+    R = len(n_valid)
+    s = rng.standard_normal((R, ld)).astype(np.float32)
+    s[3] = 3.0                                             # all equal: survivors overflow
+    s[4] = np.round(s[4] * 2) / 2                          # few values: huge tie at threshold
+    s[5] = np.linspace(-2, 2, ld, dtype=np.float32)[::-1]  # sorted descending
+    sample_pos = (np.arange(2048, dtype=np.int64) * n_valid[6]) // 2048
+    s[6, sample_pos[::2]] = 10.0 + rng.random(1024).astype(np.float32)  # 1024 < k above theta
+    s[7] = np.abs(s[7]) * 1e-30                            # tiny magnitudes (denormal range)
+    s[8, ::3] = 0.0                                        # many exact zeros
+    got = _run_topk(s, n_valid, k)
+    _expect_topk(s, n_valid, k, got)
+
+
 def test_topk_long_rows_exact():
     _case("topk long rows")
     rng = np.random.default_rng(33)
