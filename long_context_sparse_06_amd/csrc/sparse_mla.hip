@@ -78,6 +78,25 @@ __shared__ __attribute__((aligned(16))) char g_ring2[kBufBytes];
 // Partial logits exchanged between the two waves of a head block (8 floats per lane).
 __shared__ __attribute__((aligned(16))) float g_xchg[kMlaWaves][WAVE * 8];
 
+// Max / sum over lanes l and l ^ 16, and over l and l ^ 32, with the gfx950 lane-swap
+// instructions (VALU; a ds_bpermute shuffle would be an LDS round trip).
+__device__ __forceinline__ float max_x16(float v) {
+  const v2i y = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(y[0]), __int_as_float(y[1]));
+}
+__device__ __forceinline__ float max_x32(float v) {
+  const v2i y = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(y[0]), __int_as_float(y[1]));
+}
+__device__ __forceinline__ float sum_x16(float v) {
+  const v2i y = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(y[0]) + __int_as_float(y[1]);
+}
+__device__ __forceinline__ float sum_x32(float v) {
+  const v2i y = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(y[0]) + __int_as_float(y[1]);
+}
+
 template <int S>
 __device__ __forceinline__ char* ring_slot() {
   static_assert(S >= 0 && S < kNBuf, "ring slot");
@@ -100,12 +119,12 @@ struct Slot {
 // ring with global_load_lds_dwordx4 (a row is gathered once and shared by all 64 heads),
 // two tiles ahead of the one being computed, and hands a tile over by waiting for its
 // copies and one barrier (it also takes part in the compute waves' second barrier of each
-// tile, the logit exchange, so the two sides' barriers pair up).  It starts the first two tiles from the split's first 64
-// indices before building the rest of the row list, so the first gather overlaps the
-// query loads.  It never reads the ring (its only LDS reads are the row list, a different
-// variable), so the compiler never waits on copies in flight; the compute waves issue no
-// copies.  The tile loop is unrolled by the ring depth so every slot is a compile-time
-// LDS variable.
+// tile, the logit exchange, so the two sides' barriers pair up).  It starts the first two
+// tiles from the split's first 64 indices before building the rest of the row list, so
+// the first gather overlaps the query loads.  It never reads the ring (its only LDS reads
+// are the row list, a different variable), so the compiler never waits on copies in
+// flight; the compute waves issue no copies.  The tile loop is unrolled by the ring depth
+// so every slot is a compile-time LDS variable.
 template <bool PAGED, bool SPLIT>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -278,13 +297,13 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     };
 #pragma unroll
     for (int d = 0; d < VD; ++d) vfrag(d, vlo[d], vhi[d]);
+    const uint32_t live = smask[t];
     __syncthreads();  // both halves of every logit tile are in LDS
     const v4f p0 = *reinterpret_cast<const v4f*>(xpart);
     const v4f p1 = *reinterpret_cast<const v4f*>(xpart + 4);
     // Both waves of a pair add the same two halves (a + b == b + a), so their logits agree.
     const v4f sf[2] = {as[0] + p0, as[1] + p1};
     // ---- online softmax (lane holds tokens 16*st + 4*grp + i of head col)
-    const uint32_t live = smask[t];
     float s[2][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -296,8 +315,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
         mx = fmaxf(mx, s[st][i]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_x32(max_x16(mx));
     // Lazy rescaling: the reference max only moves when a logit exceeds it by more than
     // 2^8 (or on the first valid tile), so p <= 256 and the accumulators rarely rescale.
     float m_ref = m_run;
@@ -344,8 +362,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     if (t + 2 < ntiles) step(Slot<2>{}, t + 2);
   }
 
-  float l = l_run + __shfl_xor(l_run, 16);
-  l += __shfl_xor(l, 32);
+  const float l = sum_x32(sum_x16(l_run));
   // First value column of this lane in tile dt: half 0 tile dt = columns 16*dt; half 1
   // tiles 0..13 = columns 288 + 16*dt, tiles 14, 15 = columns 256 + 16*(dt - 14).
   auto vcol = [&](int dt) {
