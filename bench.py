@@ -202,6 +202,27 @@ def main():
     copy_gbs = 5 * 2 * (1 << 30) / (ca.elapsed_time(cb) * 1e6)
     del src_b, dst_b
 
+    # ---- cache append (the step before the indexer): one new token per sequence, written
+    # into scratch caches of the same row widths (timed alone; not part of the step above)
+    ap_k = torch.randn(B, sh.dI, device=dev) * 0.1
+    ap_v = torch.randn(B, sh.Dqk, device=dev).to(torch.bfloat16)
+    ap_keys = torch.empty(B, sh.dI, dtype=torch.uint8, device=dev)
+    ap_ks = torch.empty(B, dtype=torch.float32, device=dev)
+    ap_kv = torch.empty(B, sh.Dqk, dtype=torch.bfloat16, device=dev)
+    ap_seq = torch.arange(B, dtype=torch.int32, device=dev)
+    ap_pos = torch.zeros(B, dtype=torch.int32, device=dev)
+    ap_args = (ap_k, ap_v, ap_seq, ap_pos, B, sh.dI, sh.Dqk, dsa.Cache(ap_keys, ap_ks, seq_stride=1),
+               dsa.Cache(ap_kv, None, seq_stride=1))
+    dsa.dsa_cache_append(*ap_args)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(50):  # back to back: per-call cost on a busy stream
+        dsa.dsa_cache_append(*ap_args)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    append_us = a0.elapsed_time(a1) * 1e3 / 50
+    append_bytes = B * (sh.dI * 4 + sh.Dqk * 2 + 8) + B * (sh.dI + 4 + sh.Dqk * 2)
+
     # ---- CPU oracle on this host (bounded sample of the same workload)
     cpu = None
     if not args.no_cpu_baseline:
@@ -265,6 +286,8 @@ def main():
                           "frac_of_achievable": step_bytes / (copy_gbs * 1e3) / (ms_per_step * 1e3),
                           "index_frac_of_achievable": achieved / copy_gbs},
         "step_us_spread": spread,
+        "cache_append": {"us": append_us, "alg_bytes": append_bytes,
+                         "GB_s": append_bytes / (append_us * 1e3), "bound": "latency"},
         "topk_diagnostic": tie,
         "breakdown_us": {"index": idx_us, "topk": float(t_topk.mean()), "sparse_mla": float(t_mla.mean()),
                          "eager_step": (te1 - te0) * 1e6 / args.steps},

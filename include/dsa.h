@@ -12,6 +12,8 @@
  *   2. dsa_topk               the k best s per row (ties -> lower s), -1 padded
  *   3. dsa_sparse_mla_decode  MLA in MQA mode over the kept latent rows, one query
  *      dsa_sparse_mla_prefill token per sequence (decode) or every token (prefill)
+ *   and, before them, dsa_cache_append: the new token's FP8 indexer key and latent row
+ *   written into the caches.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned,
@@ -147,6 +149,28 @@ dsa_status dsa_sparse_mla_decode(dsa_dtype dt, const void* q, const dsa_cache* k
 dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,
                                   int T, int H, int Dqk, int Dv, int k, float softmax_scale,
                                   void* out, float* lse, hipStream_t stream);
+
+/*
+ * dsa_cache_append -- store each row's new token in the two caches before a step reads
+ * them: the indexer key (FP8, the pages' "FP8 index", MarkTechPost article above, two-tier
+ * pipeline) and the latent row (the joint K/V entry MLA attends over, same article,
+ * "Instantiation").  For row r the cache slot is (row_seq[r], row_pos[r]); decode writes
+ * the new token at n_valid - 1, the position dsa_index_scores and the attention read as
+ * the query's own token.
+ *
+ *   k_new  [R, d_I] fp32   the new token's indexer key, before quantisation
+ *   kv_new [R, Dqk] bf16   the new token's latent row
+ *   keys   e4m3 key cache of row width d_I with a non-NULL per-token fp32 `scale`;
+ *          WRITTEN through keys->data and keys->scale
+ *   kv     bf16 latent cache of row width Dqk; WRITTEN through kv->data
+ * Quantisation (this library's reading of "FP8"): scale = max_i |k_new[r, i]| / 448 in
+ * fp32 (1 when the key is all zero); code_i = e4m3(clamp(k_new[r, i] / scale, -448, 448))
+ * rounded to nearest, ties to even.  Rows must name distinct slots (two rows writing one
+ * slot leave either).  Limits: d_I <= 4096, Dqk <= 4096.
+ */
+dsa_status dsa_cache_append(const float* k_new, const void* kv_new, const int32_t* row_seq,
+                            const int32_t* row_pos, int R, int d_I, int Dqk, const dsa_cache* keys,
+                            const dsa_cache* kv, hipStream_t stream);
 
 /* Static text for a status code ("DSA_OK", ...); never NULL. */
 const char* dsa_status_string(dsa_status status);

@@ -17,8 +17,8 @@ import torch
 __all__ = [
     "DSAError", "DSALibraryMissing", "Cache", "F32", "BF16", "E4M3", "LIB_PATH", "lib",
     "dsa_index_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_decode",
-    "dsa_sparse_mla_decode_workspace_size", "dsa_sparse_mla_prefill", "dsa_status_string",
-    "exported_symbols",
+    "dsa_sparse_mla_decode_workspace_size", "dsa_sparse_mla_prefill", "dsa_cache_append",
+    "dsa_status_string", "exported_symbols",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
@@ -57,6 +57,8 @@ _SIGS = {
                                      _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "dsa_sparse_mla_prefill": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp]),
+    "dsa_cache_append": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, ctypes.POINTER(_Cache),
+                                ctypes.POINTER(_Cache), _vp]),
     "dsa_status_string": (ctypes.c_char_p, [_i32]),
 }
 
@@ -165,3 +167,14 @@ def dsa_sparse_mla_prefill(dt: int, q, kv, idx, T: int, H: int, Dqk: int, Dv: in
     _check("dsa_sparse_mla_prefill", lib().dsa_sparse_mla_prefill(
         dt, _ptr(q), _ptr(kv), _ptr(idx), T, H, Dqk, Dv, k, softmax_scale, _ptr(out), _ptr(lse),
         _stream(stream)))
+
+
+def dsa_cache_append(k_new, kv_new, row_seq, row_pos, R: int, d_I: int, Dqk: int, keys: Cache,
+                     kv: Cache, stream=None):
+    """Writes each row's new token into the key cache (e4m3 + fp32 scale) and the latent
+    cache, at slot (row_seq[r], row_pos[r])."""
+    ck, cv = keys._c(), kv._c()
+    _check("dsa_cache_append", lib().dsa_cache_append(
+        _ptr(k_new), _ptr(kv_new), _ptr(row_seq), _ptr(row_pos), R, d_I, Dqk, ctypes.byref(ck),
+        ctypes.byref(cv), _stream(stream)))
+

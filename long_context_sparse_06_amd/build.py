@@ -21,10 +21,12 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 ARCH = "gfx950"
 
-# Packed-fp32 VALU forms are kept out of the generated code.
+# Packed-fp32 VALU forms are kept out of the generated code; fp32 division stays
+# correctly rounded (the key quantiser's codes depend on it).
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall", "-Wno-unused-function",
 ]
 

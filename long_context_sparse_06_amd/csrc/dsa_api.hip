@@ -129,4 +129,15 @@ dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, c
                                           softmax_scale, out, lse, stream));
 }
 
+dsa_status dsa_cache_append(const float* k_new, const void* kv_new, const int32_t* row_seq,
+                            const int32_t* row_pos, int R, int d_I, int Dqk, const dsa_cache* keys,
+                            const dsa_cache* kv, hipStream_t stream) {
+  if (!k_new || !kv_new || !row_seq || !row_pos || !keys || !kv || !keys->data || !keys->scale || !kv->data)
+    return DSA_ERR_NULL;
+  if (R <= 0 || d_I <= 0 || Dqk <= 0 || d_I > 4096 || Dqk > 4096) return DSA_ERR_SHAPE;
+  if (cache_capacity(keys) <= 0 || cache_capacity(kv) <= 0) return DSA_ERR_SHAPE;
+  return launched(dsa::launch_cache_append(k_new, static_cast<const uint16_t*>(kv_new), row_seq, row_pos,
+                                           R, d_I, Dqk, view(keys), view(kv), stream));
+}
+
 }  // extern "C"

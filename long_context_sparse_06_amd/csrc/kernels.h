@@ -41,4 +41,9 @@ hipError_t launch_mla_generic(bool bf16, const void* q, const CacheView& kv, con
                               int R, int H, int Dqk, int Dv, int k, bool decode, float scale,
                               void* out, float* lse, hipStream_t s);
 
+// ---- cache append (writes through keys.data / keys.scale / kv.data)
+hipError_t launch_cache_append(const float* k_new, const uint16_t* kv_new, const int32_t* row_seq,
+                               const int32_t* row_pos, int R, int dI, int Dqk, const CacheView& keys,
+                               const CacheView& kv, hipStream_t s);
+
 }  // namespace dsa

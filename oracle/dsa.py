@@ -29,6 +29,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .formats import E4M3_TABLE
+
 
 # ----------------------------------------------------------------------------
 # tier 1: lightning indexer  ([MTP] pipeline, [MV] section 1)
@@ -130,3 +132,49 @@ def dense_causal_mla(q: np.ndarray, kv: np.ndarray, dv: int, scale: float):
 def attention_pairs(idx_sets) -> int:
     """Number of (query, key) pairs core attention touches."""
     return int(sum(len(s) for s in idx_sets))
+
+
+# ----------------------------------------------------------------------------
+# cache append: the new token's indexer key stored as FP8 ([MTP] "FP8 index")
+# ----------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def encode_e4m3(y: np.ndarray) -> np.ndarray:
+    """Finite values with |y| <= 448 -> e4m3fn codes, rounding to nearest, ties to even.
+
+    The positive finite codes 0x00..0x7E are the magnitudes in increasing order, so the
+    two neighbours of |y| are adjacent codes; on a tie the even code (even mantissa) wins.
+    The sign goes to bit 7 (so -0.0 encodes as 0x80).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    if np.any(a > E4M3_MAX) or np.any(np.isnan(y)):
+        raise ValueError("encode_e4m3 takes finite values with |y| <= 448")
+    mags = E4M3_TABLE[:0x7F]                       # codes 0x00 .. 0x7E, increasing
+    hi = np.searchsorted(mags, a, side="left")     # first code with value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(a == mags[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    neg = np.signbit(y)
+    return (code | np.where(neg, 0x80, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def quantize_key(x: np.ndarray):
+    """Per-token e4m3 quantisation of indexer keys x [..., d] (float32).
+
+    scale = amax / 448 (1 when the row is all zero), y = clamp(x / scale, -448, 448),
+    codes = e4m3(y) rounded to nearest even.  The scale and the division are float32,
+    the precision the stored scale has and the kernel computes in, so both sides take
+    the same rounding decisions.  Returns (codes uint8 [..., d], scale float32 [...]).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / scale[..., None]).astype(np.float32)
+    y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return encode_e4m3(y), scale
+

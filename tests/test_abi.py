@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_four_entry_points():
     names = declared_functions()
-    for n in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill"):
+    for n in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+              "dsa_cache_append"):
         assert n in names
     assert sorted(dsa.exported_symbols()) == names
 
@@ -72,6 +73,14 @@ def test_host_validation_paths():
     assert L.dsa_sparse_mla_decode(dsa.BF16, FAKE, ctypes.byref(kv), FAKE, 8, 128, 576, 512, 2048, 0.04, FAKE, None, FAKE, mw - 1, None) == 4
     assert L.dsa_sparse_mla_prefill(dsa.BF16, FAKE, FAKE, FAKE, 0, 128, 576, 512, 2048, 0.04, FAKE, None, None) == 2
     assert L.dsa_sparse_mla_prefill(dsa.F32, FAKE, FAKE, FAKE, 16, 4, 2000, 64, 32, 0.1, FAKE, None, None) == 6
+    # cache append
+    ks = dsa._Cache(FAKE, FAKE, None, 0, 0, 1024)
+    noscale = dsa._Cache(FAKE, None, None, 0, 0, 1024)
+    assert L.dsa_cache_append(FAKE, FAKE, FAKE, FAKE, 4, 128, 576, ctypes.byref(noscale), ctypes.byref(kv), None) == 1
+    assert L.dsa_cache_append(None, FAKE, FAKE, FAKE, 4, 128, 576, ctypes.byref(ks), ctypes.byref(kv), None) == 1
+    assert L.dsa_cache_append(FAKE, FAKE, FAKE, FAKE, 0, 128, 576, ctypes.byref(ks), ctypes.byref(kv), None) == 2
+    assert L.dsa_cache_append(FAKE, FAKE, FAKE, FAKE, 4, 8192, 576, ctypes.byref(ks), ctypes.byref(kv), None) == 2
+    assert L.dsa_cache_append(FAKE, FAKE, FAKE, FAKE, 4, 128, 576, ctypes.byref(ks), ctypes.byref(bad), None) == 2
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -130,6 +130,63 @@ def test_index_scores_generic_fp32():
         parity.check_scores(got[t, : t + 1], ref, ref_abs, f"t={t}")
 
 
+# ----------------------------------------------------------------------------- cache append
+@pytest.mark.parametrize("paged", [False, True])
+def test_cache_append_matches_oracle_quantiser(paged):
+    """The new token's key lands as oracle.quantize_key's codes and scale (bit-exact), its
+    latent row as given, and nothing else in either cache changes."""
+    import long_context_sparse_06_amd as dsa
+    _case(f"cache_append paged={paged}")
+    rng = np.random.default_rng(41)
+    lengths = np.array([100, 64, 65, 1, 4000, 257])
+    B, dI, D, ps = len(lengths), FULL.dI, FULL.Dqk, 64
+    k_new = (rng.standard_normal((B, dI)) * 0.3).astype(np.float32)
+    k_new[1] = 0.0                                                    # all zero: scale 1
+    ties = np.array([448.0, 1.0625, 1.1875, 432.0, 1.5 * 2.0 ** -9, 7.5 * 2.0 ** -9, -1.0625, -0.0],
+                    dtype=np.float32)
+    k_new[2] = rng.choice([-3.0, -1.0, 0.5, 2.0], size=dI).astype(np.float32)
+    k_new[2, : len(ties)] = ties                                      # scale 1: exact ties
+    k_new[3] *= np.float32(1e-30)                                     # tiny keys
+    k_new[4] *= np.float32(1e30)                                      # huge keys
+    k_new[5, ::7] = -0.0
+    kv_new = datagen.to_bf16_bits(rng.standard_normal((B, D)).astype(np.float32))
+    seq = np.arange(B, dtype=np.int32)
+    pos = (lengths - 1).astype(np.int32)
+    if paged:
+        table, n_pages = datagen.make_block_table(rng, lengths, ps)
+        keys0 = np.full((n_pages, ps, dI), 0x5A, dtype=np.uint8)
+        ks0 = np.full((n_pages, ps), np.nan, dtype=np.float32)
+        kv0 = np.full((n_pages, ps, D), 0x1234, dtype=np.uint16)
+        slot = lambda b: (int(table[b, pos[b] // ps]), int(pos[b] % ps))
+    else:
+        Lmax = int(lengths.max())
+        keys0 = np.full((B, Lmax, dI), 0x5A, dtype=np.uint8)
+        ks0 = np.full((B, Lmax), np.nan, dtype=np.float32)
+        kv0 = np.full((B, Lmax, D), 0x1234, dtype=np.uint16)
+        slot = lambda b: (b, int(pos[b]))
+    keys, ks, kv = tensor(keys0), tensor(ks0), tensor(kv0)
+    bt = tensor(table) if paged else None
+    stride = 0 if paged else int(keys0.shape[1])
+    dsa.dsa_cache_append(tensor(k_new), tensor(kv_new), tensor(seq), tensor(pos), B, dI, D,
+                         dsa.Cache(keys, ks, bt, ps if paged else 0, stride),
+                         dsa.Cache(kv, None, bt, ps if paged else 0, stride))
+    codes, scale = oracle.quantize_key(k_new)
+    exp_k, exp_s, exp_v = keys0.copy(), ks0.copy(), kv0.copy()
+    for b in range(B):
+        i, j = slot(b)
+        exp_k[i, j], exp_s[i, j], exp_v[i, j] = codes[b], scale[b], kv_new[b]
+    got_k = keys.cpu().numpy()
+    got_s = ks.cpu().numpy()
+    got_v = kv.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(B):
+        i, j = slot(b)
+        assert np.array_equal(got_k[i, j], codes[b]), f"row {b}: codes differ at {np.nonzero(got_k[i, j] != codes[b])[0][:8]}"
+        assert got_s[i, j].view(np.uint32) == scale[b].view(np.uint32), f"row {b}: scale {got_s[i, j]} vs {scale[b]}"
+    assert np.array_equal(got_k, exp_k)
+    assert np.array_equal(np.isnan(got_s), np.isnan(exp_s)) and np.array_equal(got_s[~np.isnan(exp_s)], exp_s[~np.isnan(exp_s)])
+    assert np.array_equal(got_v, exp_v)
+
+
 # ----------------------------------------------------------------------------- top-k
 def _run_topk(scores_np, n_valid, k):
     import long_context_sparse_06_amd as dsa

@@ -10,7 +10,11 @@ Each pin is chosen so that a plausible mistake in the oracle fails it:
   * sparse MLA vs a hand-worked golden case, closed forms (single row, zero
     query, two rows), torch's scaled_dot_product_attention for the dense
     causal case (k >= L), and permutation invariance;
-  * the O(Lk) pair count vs its closed form.
+  * the O(Lk) pair count vs its closed form;
+  * the e4m3 encoder vs the decoder on every code, hand-worked ties (to even) and
+    subnormals, and torch's float8_e4m3fn cast; the key quantiser vs its closed-form
+    consequences (the largest magnitude maps to +-448, zero rows keep scale 1, the
+    dequantised value is within half an e4m3 step of the input).
 """
 import itertools
 import json
@@ -48,6 +52,49 @@ def test_e4m3_closed_forms():
     assert d[2] == 2.0 ** -6             # smallest normal
     assert d[3] == 1.0 and d[4] == -1.0 and d[5] == 0.0
     assert d[6] == 7 / 8 * 2.0 ** -6     # largest subnormal
+
+
+def test_e4m3_encoder_inverts_the_decoder_on_every_finite_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(oracle.encode_e4m3(decode_e4m3(codes)), codes)
+
+
+def test_e4m3_encoder_ties_go_to_even_and_subnormals_by_hand():
+    # midpoints between neighbouring codes, worked by hand from the format definition
+    cases = {1.0625: 0x38,          # between 1.0 (0x38) and 1.125 (0x39): even 0x38
+             1.1875: 0x3A,          # between 1.125 (0x39) and 1.25 (0x3A): even 0x3A
+             1.5 * 2.0 ** -9: 0x02,  # between subnormals 1 and 2 (x 2^-9): even 2
+             2.5 * 2.0 ** -9: 0x02,  # between 2 and 3: even 2
+             7.5 * 2.0 ** -9: 0x08,  # between the largest subnormal and 2^-6: 0x08
+             432.0: 0x7E,           # between 416 (0x7D) and 448 (0x7E): even 0x7E
+             0.3 * 2.0 ** -9: 0x00,  # below half the smallest subnormal: zero
+             -1.0625: 0xB8}
+    got = oracle.encode_e4m3(np.array(list(cases.keys())))
+    assert got.tolist() == list(cases.values())
+
+
+def test_e4m3_encoder_matches_torch_cast():
+    rng = np.random.default_rng(5)
+    y = np.concatenate([rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 0.01,
+                        rng.standard_normal(2000) * 2.0 ** -8]).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.encode_e4m3(y), ref)
+
+
+def test_quantize_key_closed_forms():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((50, 128)).astype(np.float32)
+    x[3] = 0.0
+    x[4] = 1e-30
+    codes, scale = oracle.quantize_key(x)
+    assert scale.dtype == np.float32 and scale[3] == 1.0 and (codes[3] == 0).all()
+    amax_at = np.argmax(np.abs(x), axis=1)
+    top = codes[np.arange(50), amax_at]
+    assert ((top & 0x7F) == 0x7E)[np.arange(50) != 3].all()          # +-448
+    back = decode_e4m3(codes) * scale[:, None].astype(np.float64)
+    err = np.abs(back - x)
+    step = np.maximum(np.abs(x) * 2.0 ** -4, scale[:, None] * 2.0 ** -10)  # half an e4m3 step
+    assert (err <= step * (1 + 1e-6)).all()
 
 
 def test_bf16_decoder_matches_torch():
