@@ -349,6 +349,27 @@ def prefill(args):
     idx_flops = float(n.sum()) * sh.HI * sh.dI * 2
     kept = np.minimum(n, sh.k)
     mla_flops = float(kept.sum()) * sh.H * (sh.Dqk + sh.Dv) * 2
+    # Short prefill (T = 2048, every earlier token kept): sparse gather vs the dense masked form.
+    Ts = 2048
+    sinp = datagen.make_prefill(Ts, sh, datagen.seed_for(4) + 1)
+    sq = upload_prefill(sinp, dev)
+    del sinp
+    sidx = torch.full((Ts, sh.k), -1, dtype=torch.int32, device=dev)
+    ar = torch.arange(sh.k, dtype=torch.int32, device=dev)
+    sidx = torch.where(ar[None, :] <= torch.arange(Ts, device=dev)[:, None], ar[None, :], sidx).contiguous()
+    so = torch.empty(Ts, sh.H, sh.Dv, dtype=torch.bfloat16, device=dev)
+    sl = torch.empty(Ts, sh.H, dtype=torch.float32, device=dev)
+    short = {}
+    for name, fn in (("sparse", dsa.dsa_sparse_mla_prefill), ("masked", dsa.dsa_masked_mla_prefill)):
+        fn(dsa.BF16, sq.q, sq.kv, sidx, Ts, sh.H, sh.Dqk, sh.Dv, sh.k, scale, so, sl)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            fn(dsa.BF16, sq.q, sq.kv, sidx, Ts, sh.H, sh.Dqk, sh.Dv, sh.k, scale, so, sl)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        short[name + "_ms"] = e0.elapsed_time(e1) / 5
+    del sq, sidx, so, sl
     idx_tf = idx_flops / (t_idx * 1e-3) / 1e12
     mla_tf = mla_flops / (t_mla * 1e-3) / 1e12
     out = {
@@ -365,6 +386,7 @@ def prefill(args):
         "config": {"workload": cfg["name"], "tokens": T, "top_k": sh.k, "heads": sh.H, "latent": sh.Dqk,
                    "value_dim": sh.Dv, "indexer_heads": sh.HI, "indexer_dim": sh.dI},
         "stages_ms": {"index": t_idx, "topk": t_topk, "sparse_mla": t_mla},
+        "short_prefill_t2048_attention": short,
         "roofline": {
             "index": {"bound": "mfma", "achieved": idx_tf, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                       "frac": idx_tf / FP8_PEAK_TFLOPS, "alg_flops": idx_flops},

@@ -13,7 +13,8 @@
  *   3. dsa_sparse_mla_decode  MLA in MQA mode over the kept latent rows, one query
  *      dsa_sparse_mla_prefill token per sequence (decode) or every token (prefill)
  *   and, before them, dsa_cache_append: the new token's FP8 indexer key and latent row
- *   written into the caches.
+ *   written into the caches; dsa_masked_mla_prefill: step 3 of a prefill in dense masked
+ *   form, for short sequences.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned,
@@ -147,6 +148,22 @@ dsa_status dsa_sparse_mla_decode(dsa_dtype dt, const void* q, const dsa_cache* k
  * dt and shape rules as for dsa_sparse_mla_decode.
  */
 dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,
+                                  int T, int H, int Dqk, int Dv, int k, float softmax_scale,
+                                  void* out, float* lse, hipStream_t stream);
+
+/*
+ * dsa_masked_mla_prefill -- the same result as dsa_sparse_mla_prefill, computed in the
+ * dense "masked" form the pages name for short prefill (MarkTechPost article above, "Costs
+ * vs. position (128k)": prefill benefits through a masked MHA simulation at short lengths):
+ * row t runs over the contiguous positions 0..t in 32-row tiles and masks every position
+ * not in its kept set S_t = { idx[t, j] : 0 <= idx[t, j] <= t } (other entries are ignored).
+ * No row gather, but the cost grows with t rather than |S_t|: it pays while t + 1 is
+ * within a small multiple of k.
+ *
+ *   arguments, layouts, dtypes and limits as dsa_sparse_mla_prefill; T <= 65536.
+ * Shapes off the bf16 fast path are served by the same generic kernel as the sparse call.
+ */
+dsa_status dsa_masked_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,
                                   int T, int H, int Dqk, int Dv, int k, float softmax_scale,
                                   void* out, float* lse, hipStream_t stream);
 

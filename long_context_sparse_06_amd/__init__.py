@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "DSAError", "DSALibraryMissing", "Cache", "F32", "BF16", "E4M3", "LIB_PATH", "lib",
     "dsa_index_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_decode",
-    "dsa_sparse_mla_decode_workspace_size", "dsa_sparse_mla_prefill", "dsa_cache_append",
+    "dsa_sparse_mla_decode_workspace_size", "dsa_sparse_mla_prefill", "dsa_masked_mla_prefill",
+    "dsa_cache_append",
     "dsa_status_string", "exported_symbols",
 ]
 
@@ -56,6 +57,8 @@ _SIGS = {
     "dsa_sparse_mla_decode": (_i32, [_i32, _vp, ctypes.POINTER(_Cache), _vp, _i32, _i32, _i32, _i32,
                                      _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "dsa_sparse_mla_prefill": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                      _vp, _vp]),
+    "dsa_masked_mla_prefill": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp]),
     "dsa_cache_append": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, ctypes.POINTER(_Cache),
                                 ctypes.POINTER(_Cache), _vp]),
@@ -177,4 +180,12 @@ def dsa_cache_append(k_new, kv_new, row_seq, row_pos, R: int, d_I: int, Dqk: int
     _check("dsa_cache_append", lib().dsa_cache_append(
         _ptr(k_new), _ptr(kv_new), _ptr(row_seq), _ptr(row_pos), R, d_I, Dqk, ctypes.byref(ck),
         ctypes.byref(cv), _stream(stream)))
+
+
+def dsa_masked_mla_prefill(dt: int, q, kv, idx, T: int, H: int, Dqk: int, Dv: int, k: int,
+                           softmax_scale: float, out, lse=None, stream=None):
+    """dsa_sparse_mla_prefill's result in dense masked form (positions 0..t, kept set as mask)."""
+    _check("dsa_masked_mla_prefill", lib().dsa_masked_mla_prefill(
+        dt, _ptr(q), _ptr(kv), _ptr(idx), T, H, Dqk, Dv, k, softmax_scale, _ptr(out), _ptr(lse),
+        _stream(stream)))
 

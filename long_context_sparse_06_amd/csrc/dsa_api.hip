@@ -129,6 +129,23 @@ dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, c
                                           softmax_scale, out, lse, stream));
 }
 
+dsa_status dsa_masked_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,
+                                  int T, int H, int Dqk, int Dv, int k, float softmax_scale, void* out,
+                                  float* lse, hipStream_t stream) {
+  dsa_status st = mla_check(dt, q, kv, idx, T, H, Dqk, Dv, k, out);
+  if (st != DSA_OK) return st;
+  if (T > 65536) return DSA_ERR_SHAPE;
+  if (mla_fast(dt, H, Dqk, Dv))
+    return launched(dsa::launch_mla_bf16_masked(static_cast<const uint16_t*>(q),
+                                                static_cast<const uint16_t*>(kv), idx, T, H, k,
+                                                softmax_scale, static_cast<uint16_t*>(out), lse, stream));
+  // Other shapes: the generic kernel computes the same attention from the index list.
+  const dsa::CacheView v{kv, nullptr, nullptr, 0, 0, (int64_t)T};
+  if ((st = mla_generic_ok(Dqk, k)) != DSA_OK) return st;
+  return launched(dsa::launch_mla_generic(dt == DSA_BF16, q, v, idx, T, H, Dqk, Dv, k, false,
+                                          softmax_scale, out, lse, stream));
+}
+
 dsa_status dsa_cache_append(const float* k_new, const void* kv_new, const int32_t* row_seq,
                             const int32_t* row_pos, int R, int d_I, int Dqk, const dsa_cache* keys,
                             const dsa_cache* kv, hipStream_t stream) {

@@ -37,6 +37,9 @@ size_t mla_decode_workspace_bytes(int B, int H, int Dv, int k);
 hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t* idx, int R,
                            int H, int k, bool decode, float scale, uint16_t* out, float* lse,
                            void* ws, size_t ws_bytes, hipStream_t s);
+// Prefill attention in its dense "masked" form: row t over positions 0..t, masked to idx[t, :].
+hipError_t launch_mla_bf16_masked(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int T,
+                                  int H, int k, float scale, uint16_t* out, float* lse, hipStream_t s);
 hipError_t launch_mla_generic(bool bf16, const void* q, const CacheView& kv, const int32_t* idx,
                               int R, int H, int Dqk, int Dv, int k, bool decode, float scale,
                               void* out, float* lse, hipStream_t s);

@@ -77,6 +77,10 @@ __shared__ __attribute__((aligned(16))) char g_ring1[kBufBytes];
 __shared__ __attribute__((aligned(16))) char g_ring2[kBufBytes];
 // Partial logits exchanged between the two waves of a head block (8 floats per lane).
 __shared__ __attribute__((aligned(16))) float g_xchg[kMlaWaves][WAVE * 8];
+// Tiles this workgroup actually runs: up to the last kept token of its range (index lists
+// are -1 padded at the end when a row has fewer than k candidates); set by the copy wave
+// before the first hand-over.
+__shared__ int g_ntiles;
 
 // Max / sum over lanes l and l ^ 16, and over l and l ^ 32, with the gfx950 lane-swap
 // instructions (VALU; a ds_bpermute shuffle would be an LDS round trip).
@@ -125,7 +129,11 @@ struct Slot {
 // are the row list, a different variable), so the compiler never waits on copies in
 // flight; the compute waves issue no copies.  The tile loop is unrolled by the ring depth
 // so every slot is a compile-time LDS variable.
-template <bool PAGED, bool SPLIT>
+//
+// MASKED (prefill only): row t attends over the contiguous positions 0..t, each tile's live
+// mask set from the bits of the kept set idx[t, :] -- the dense "masked" form of the same
+// attention (no row-list gather; contiguous tiles).
+template <bool PAGED, bool SPLIT, bool MASKED = false>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ table, int max_pages, int page_size, int64_t seq_stride,
@@ -133,20 +141,21 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml, int n_split, int tok_per_split) {
   extern __shared__ int srow[];  // [tok_per_split] cache row of each kept token, -1 = none;
-                                 // then [tiles] bit mask of each tile's live tokens
+                                 // then [tiles] bit mask of each tile's live tokens (MASKED:
+                                 // the masks only)
   const int HG = H / kHeadsPerWg;
   int bid = blockIdx.x;
   const int sp = bid % n_split;
   bid /= n_split;
   const int hg = bid % HG;
   const int r = bid / HG;
-  const int t_begin = sp * tok_per_split;
-  const int t_end = min(k, t_begin + tok_per_split);
+  const int t_begin = MASKED ? 0 : sp * tok_per_split;
+  const int t_end = MASKED ? r + 1 : min(k, t_begin + tok_per_split);
   const int n_tok = t_end > t_begin ? t_end - t_begin : 0;
   const int ntiles = (n_tok + kTok - 1) / kTok;
   const int seq = decode ? r : 0;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  uint32_t* smask = reinterpret_cast<uint32_t*>(srow + tok_per_split);
+  uint32_t* smask = reinterpret_cast<uint32_t*>(MASKED ? srow : srow + tok_per_split);
 
   if (w == kMlaWaves) {
     // ---------------------------------------------------------------- copy wave
@@ -170,11 +179,32 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
         __builtin_amdgcn_global_load_lds((const void*)(src + 8 * j),
                                          (lds_void*)(uintptr_t)(lds_offset(dst) + j * kBlock), 16, 0, 0);
     };
+    int last = MASKED ? n_tok - 1 : -1;  // last kept token of the range (uniform)
+    if (MASKED) {
+      // Live masks from the kept set (positions outside 0..r are ignored), then tiles 0
+      // and 1 of the contiguous positions.
+      for (int i = lane; i < ntiles; i += WAVE) smask[i] = 0u;
+      const int32_t* krow = idx + (int64_t)r * k;
+      constexpr int U = 8;
+      for (int j0 = 0; j0 < k; j0 += U * WAVE) {
+        int id[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) id[u] = krow[min(j0 + u * WAVE + lane, k - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int s = id[u];
+          if (j0 + u * WAVE + lane < k && s >= 0 && s < n_tok) atomicOr(&smask[s >> 5], 1u << (s & 31));
+        }
+      }
+      if (ntiles > 0) issue_row((lane & 31) < n_tok ? (lane & 31) : -1, g_ring0);
+      if (ntiles > 1) issue_row(32 + (lane & 31) < n_tok ? 32 + (lane & 31) : -1, g_ring1);
+    } else {
     // Tiles 0 and 1 straight from the first 64 indices (token = lane).
     {
       const int v = lane < n_tok ? irow[min(lane, n_tok - 1)] : -1;
       const int row = resolve(v);
       const uint64_t live = ballot(row >= 0);
+      if (live) last = 63 - (int)__builtin_clzll(live);
       if (lane < n_tok) srow[lane] = row;
       if (lane == 0) {
         if (ntiles > 0) smask[0] = (uint32_t)live;
@@ -200,28 +230,35 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
         const int i = i0 + u * WAVE + lane;
         const int row = resolve(id[u]);
         const uint64_t live = ballot(row >= 0);
+        if (live) last = i0 + u * WAVE + 63 - (int)__builtin_clzll(live);
         if (i < n_tok) srow[i] = row;
         const int t0 = (i0 + u * WAVE) / kTok;
         if (lane == 0 && t0 < ntiles) smask[t0] = (uint32_t)live;
         if (lane == 0 && t0 + 1 < ntiles) smask[t0 + 1] = (uint32_t)(live >> 32);
       }
     }
+    }
+    // Tiles run: through the last kept token, at least one (tiles 0 and 1 are already in
+    // flight; the last hand-over drains whatever was issued).
+    const int nt = ntiles == 0 ? 0 : max(1, min(ntiles, (last + kTok) / kTok));
+    if (lane == 0) g_ntiles = nt;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the count is in LDS before the barrier
     auto row_of_tile = [&](int t) {
       const int tok = t * kTok + (lane & 31);
-      return tok < n_tok ? srow[tok] : -1;
+      return tok < n_tok ? (MASKED ? tok : srow[tok]) : -1;
     };
     auto hand = [&](auto slot, int t) {
       constexpr int S = decltype(slot)::value;
-      if (t + 1 < ntiles) wait_vmcnt<kDmaPerTile>();  // tile t landed, t+1 may be in flight
+      if (t + 1 < nt) wait_vmcnt<kDmaPerTile>();  // tile t landed, t+1 may be in flight
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();                    // hand tile t to the compute waves
-      if (t + 2 < ntiles) issue_row(row_of_tile(t + 2), ring_slot<(S + 2) % kNBuf>());
+      if (t + 2 < nt) issue_row(row_of_tile(t + 2), ring_slot<(S + 2) % kNBuf>());
       __builtin_amdgcn_s_barrier();  // the compute waves' logit exchange (barriers must pair up)
     };
-    for (int t = 0; t < ntiles; t += kNBuf) {
+    for (int t = 0; t < nt; t += kNBuf) {
       hand(Slot<0>{}, t);
-      if (t + 1 < ntiles) hand(Slot<1>{}, t + 1);
-      if (t + 2 < ntiles) hand(Slot<2>{}, t + 2);
+      if (t + 1 < nt) hand(Slot<1>{}, t + 1);
+      if (t + 2 < nt) hand(Slot<2>{}, t + 2);
     }
     return;
   }
@@ -356,10 +393,16 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
     }
   };
 
-  for (int t = 0; t < ntiles; t += kNBuf) {
-    step(Slot<0>{}, t);
-    if (t + 1 < ntiles) step(Slot<1>{}, t + 1);
-    if (t + 2 < ntiles) step(Slot<2>{}, t + 2);
+  if (ntiles > 0) {
+    step(Slot<0>{}, 0);
+    const int nt = g_ntiles;  // written by the copy wave before the first hand-over
+    if (1 < nt) step(Slot<1>{}, 1);
+    if (2 < nt) step(Slot<2>{}, 2);
+    for (int t = kNBuf; t < nt; t += kNBuf) {
+      step(Slot<0>{}, t);
+      if (t + 1 < nt) step(Slot<1>{}, t + 1);
+      if (t + 2 < nt) step(Slot<2>{}, t + 2);
+    }
   }
 
   const float l = sum_x32(sum_x16(l_run));
@@ -588,6 +631,16 @@ hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t
     mla_combine_kernel<8><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
   else
     mla_combine_kernel<16><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_bf16_masked(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int T,
+                                  int H, int k, float scale, uint16_t* out, float* lse, hipStream_t s) {
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  const unsigned grid = (unsigned)((int64_t)T * (H / kHeadsPerWg));
+  const size_t lds = sizeof(uint32_t) * (size_t)((T + kTok - 1) / kTok);  // one live mask per tile
+  mla_bf16_kernel<false, false, true><<<grid, kMlaThreads, lds, s>>>(
+      q, kv, nullptr, 0, 1, (int64_t)T, idx, k, H, 0, scale_log2, out, lse, nullptr, nullptr, 1, 0);
   return hipGetLastError();
 }
 
