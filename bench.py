@@ -3,9 +3,11 @@
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
     python bench.py --mode prefill [--steps K]      (workload 4, reported, not the headline)
 
-A step is the whole hot path for one new token per sequence: dsa_index_scores (FP8
-lightning indexer over every cached token) -> dsa_topk (k = 2048) -> dsa_sparse_mla_decode
-(MLA in MQA mode over the kept rows, split-KV combine included).  The default workload is
+A step is the whole hot path for one new token per sequence: the FP8 lightning indexer
+over every cached token and the top-k (k = 2048) -- issued as the one call dsa_index_topk,
+the same result as dsa_index_scores -> dsa_topk -- then dsa_sparse_mla_decode (MLA in MQA
+mode over the kept rows, split-KV combine included).  Per-stage times come from an eager
+pass that issues the three calls separately.  The default workload is
 batch 8 x 131072 context (128 query heads, 576-wide bf16 latent rows, 64 x 128 e4m3
 indexer), synthetic N(0,1)/sqrt(d) data (seed 1003).  Inputs are resident in HBM before
 timing starts; `--copies` distinct copies of the caches are rotated step by step so the
@@ -202,6 +204,33 @@ def main():
     copy_gbs = 5 * 2 * (1 << 30) / (ca.elapsed_time(cb) * 1e6)
     del src_b, dst_b
 
+    # ---- the fused index + top-k call beside the two separate calls (eager, events)
+    st0 = steps[0]
+    fw = dsa.dsa_index_topk_workspace_size(B, st0.ld, st0.k)
+    fws = torch.empty(fw, dtype=torch.uint8, device=dev)
+    fidx = torch.empty_like(st0.idx)
+
+    def fused():
+        dsa.dsa_index_topk(st0.idx_dt, st0.q_idx, st0.q_scale, st0.w, st0.keys, st0.row_seq,
+                           st0.row_pos, B, st0.HI, st0.dI, st0.k, fidx, fws, fw)
+
+    def separate():
+        st0.index()
+        st0.topk()
+
+    fused_cmp = {}
+    for name, fn in (("fused_us", fused), ("separate_us", separate)):
+        fn()
+        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a, b in fe:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        fused_cmp[name] = float(np.mean([a.elapsed_time(b) for a, b in fe[2:]]) * 1e3)
+    fused_cmp["same_result"] = bool(torch.equal(fidx, st0.idx))
+    del fws
+
     # ---- cache append (the step before the indexer): one new token per sequence, written
     # into scratch caches of the same row widths (timed alone; not part of the step above)
     ap_k = torch.randn(B, sh.dI, device=dev) * 0.1
@@ -294,6 +323,7 @@ def main():
                           "frac_of_achievable": step_bytes / (copy_gbs * 1e3) / (ms_per_step * 1e3),
                           "index_frac_of_achievable": achieved / copy_gbs},
         "step_us_spread": spread,
+        "index_topk_fused_vs_separate": fused_cmp,
         "cache_append": {"us": append_us, "alg_bytes": append_bytes,
                          "GB_s": append_bytes / (append_us * 1e3), "bound": "latency"},
         "topk_diagnostic": tie,

@@ -13,8 +13,8 @@
  *   3. dsa_sparse_mla_decode  MLA in MQA mode over the kept latent rows, one query
  *      dsa_sparse_mla_prefill token per sequence (decode) or every token (prefill)
  *   and, before them, dsa_cache_append: the new token's FP8 indexer key and latent row
- *   written into the caches; dsa_masked_mla_prefill: step 3 of a prefill in dense masked
- *   form, for short sequences.
+ *   written into the caches; dsa_index_topk: steps 1 and 2 in one call;
+ *   dsa_masked_mla_prefill: step 3 of a prefill in dense masked form, for short sequences.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned,
@@ -150,6 +150,27 @@ dsa_status dsa_sparse_mla_decode(dsa_dtype dt, const void* q, const dsa_cache* k
 dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,
                                   int T, int H, int Dqk, int Dv, int k, float softmax_scale,
                                   void* out, float* lse, hipStream_t stream);
+
+/*
+ * dsa_index_topk -- dsa_index_scores followed by dsa_topk in one call (the pages' "FP8 index
+ * -> top-k selection" as one stage), with n_valid[r] = row_pos[r] + 1.  The result is exactly
+ * that of the two calls (same scores, same selection rule).  Fused: the indexer also stores
+ * each long row's 2048 evenly spaced sample scores contiguously, where the top-k's threshold
+ * search reads them as one block instead of gathering them from the score row.  Scores,
+ * sample and top-k workspace all live in `ws`.
+ *
+ *   arguments as dsa_index_scores (the keys cache's capacity plays the role of ld) and dsa_topk
+ *   idx [R, k] int32 output, as dsa_topk
+ *   ws    device workspace of at least dsa_index_topk_workspace_size(R, capacity, k) bytes;
+ *         on return its first R * capacity * 4 bytes hold the index scores as dsa_index_scores
+ *         would write them with ld = capacity (fp32 [R, capacity])
+ * Limits: as the two calls; capacity <= 2^24.
+ */
+size_t dsa_index_topk_workspace_size(int R, int64_t n_max, int k);
+dsa_status dsa_index_topk(dsa_dtype dt, const void* q, const float* q_scale, const float* w,
+                          const dsa_cache* keys, const int32_t* row_seq, const int32_t* row_pos,
+                          int R, int H_I, int d_I, int k, int32_t* idx, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
 
 /*
  * dsa_masked_mla_prefill -- the same result as dsa_sparse_mla_prefill, computed in the

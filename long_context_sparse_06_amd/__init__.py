@@ -18,6 +18,7 @@ __all__ = [
     "DSAError", "DSALibraryMissing", "Cache", "F32", "BF16", "E4M3", "LIB_PATH", "lib",
     "dsa_index_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_decode",
     "dsa_sparse_mla_decode_workspace_size", "dsa_sparse_mla_prefill", "dsa_masked_mla_prefill",
+    "dsa_index_topk", "dsa_index_topk_workspace_size",
     "dsa_cache_append",
     "dsa_status_string", "exported_symbols",
 ]
@@ -58,6 +59,9 @@ _SIGS = {
                                      _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "dsa_sparse_mla_prefill": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp]),
+    "dsa_index_topk_workspace_size": (_sz, [_i32, _i64, _i32]),
+    "dsa_index_topk": (_i32, [_i32, _vp, _vp, _vp, ctypes.POINTER(_Cache), _vp, _vp, _i32, _i32, _i32,
+                              _i32, _vp, _vp, _sz, _vp]),
     "dsa_masked_mla_prefill": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp]),
     "dsa_cache_append": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, ctypes.POINTER(_Cache),
@@ -188,4 +192,19 @@ def dsa_masked_mla_prefill(dt: int, q, kv, idx, T: int, H: int, Dqk: int, Dv: in
     _check("dsa_masked_mla_prefill", lib().dsa_masked_mla_prefill(
         dt, _ptr(q), _ptr(kv), _ptr(idx), T, H, Dqk, Dv, k, softmax_scale, _ptr(out), _ptr(lse),
         _stream(stream)))
+
+
+def dsa_index_topk_workspace_size(R: int, n_max: int, k: int) -> int:
+    return int(lib().dsa_index_topk_workspace_size(R, n_max, k))
+
+
+def dsa_index_topk(dt: int, q, q_scale, w, keys: Cache, row_seq, row_pos, R: int, H_I: int,
+                   d_I: int, k: int, idx, ws, ws_bytes: int = 0, stream=None):
+    """Index scores and top-k in one call (n_valid = row_pos + 1); scores live in `ws`."""
+    if ws is not None and not ws_bytes:
+        ws_bytes = ws.numel() * ws.element_size()
+    c = keys._c()
+    _check("dsa_index_topk", lib().dsa_index_topk(
+        dt, _ptr(q), _ptr(q_scale), _ptr(w), ctypes.byref(c), _ptr(row_seq), _ptr(row_pos), R, H_I,
+        d_I, k, _ptr(idx), _ptr(ws), ws_bytes, _stream(stream)))
 

@@ -129,6 +129,56 @@ dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, c
                                           softmax_scale, out, lse, stream));
 }
 
+namespace {
+struct FusedWs {
+  size_t scores, samp, topk, total;
+};
+FusedWs fused_ws(int R, int64_t cap, int k) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  FusedWs L{};
+  L.scores = 0;
+  L.samp = up(sizeof(float) * (size_t)R * (size_t)cap);
+  L.topk = L.samp + up(sizeof(float) * (size_t)R * 2048);
+  L.total = L.topk + up(dsa::topk_workspace_bytes(R, cap, k));
+  return L;
+}
+}  // namespace
+
+size_t dsa_index_topk_workspace_size(int R, int64_t n_max, int k) {
+  if (R <= 0 || n_max <= 0 || k <= 0) return 0;
+  return fused_ws(R, n_max, k).total;
+}
+
+dsa_status dsa_index_topk(dsa_dtype dt, const void* q, const float* q_scale, const float* w,
+                          const dsa_cache* keys, const int32_t* row_seq, const int32_t* row_pos,
+                          int R, int H_I, int d_I, int k, int32_t* idx, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (!q || !w || !keys || !keys->data || !row_seq || !row_pos || !idx) return DSA_ERR_NULL;
+  if (dt != DSA_E4M3 && dt != DSA_F32) return DSA_ERR_DTYPE;
+  if (R <= 0 || H_I <= 0 || d_I <= 0 || R > 65535 || k <= 0 || k > 16384) return DSA_ERR_SHAPE;
+  const int64_t cap = cache_capacity(keys);
+  if (cap <= 0 || cap > (int64_t(1) << 24) || !dsa::topk_shape_ok(R, cap)) return DSA_ERR_SHAPE;
+  if ((int64_t)H_I * d_I > 16384) return DSA_ERR_UNSUPPORTED;
+  const FusedWs L = fused_ws(R, cap, k);
+  if (!ws || ws_bytes < L.total) return DSA_ERR_WORKSPACE;
+  char* b = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(b + L.scores);
+  float* samp = reinterpret_cast<float*>(b + L.samp);
+  void* tws = b + L.topk;
+  const dsa::CacheView kv = view(keys);
+  hipError_t e;
+  if (dt == DSA_E4M3 && H_I == 64 && d_I == 128) {
+    e = dsa::launch_index_fp8_h64d128(static_cast<const uint8_t*>(q), q_scale, w, kv, row_seq, row_pos,
+                                      R, cap, scores, cap, stream, samp, dsa::topk_long_row_min());
+    if (e != hipSuccess) return DSA_ERR_LAUNCH;
+    return launched(dsa::launch_topk(scores, cap, row_pos, R, k, idx, tws, stream, samp, 1));
+  }
+  e = dsa::launch_index_generic(dt == DSA_E4M3, q, q_scale, w, kv, row_seq, row_pos, R, H_I, d_I, cap,
+                                scores, cap, stream);
+  if (e != hipSuccess) return DSA_ERR_LAUNCH;
+  return launched(dsa::launch_topk(scores, cap, row_pos, R, k, idx, tws, stream, nullptr, 1));
+}
+
 dsa_status dsa_masked_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,
                                   int T, int H, int Dqk, int Dv, int k, float softmax_scale, void* out,
                                   float* lse, hipStream_t stream) {

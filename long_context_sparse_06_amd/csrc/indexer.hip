@@ -70,13 +70,20 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ qr, const
 // butterfly of gfx950 lane swaps (v_permlane32_swap, v_permlane16_swap) then adds the four
 // partial sums of each group and leaves group g's totals in lanes 16*g .. 16*g+15, so the 64
 // scores of the trip leave in one coalesced 256-byte store.
-template <bool PAGED>
+//
+// SAMPLE (the fused index + top-k call): rows longer than samp_min_n also store the scores
+// at the evenly spaced positions (i * n) / kIdxSample, i < kIdxSample, contiguously in
+// samp[r, i], where the top-k's threshold search reads them as one 8 KB block instead of
+// 2048 scattered scores of the row.
+constexpr int kIdxSample = 2048;
+template <bool PAGED, bool SAMPLE = false>
 __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kdata, const float* __restrict__ kscale,
     const int32_t* __restrict__ table, int max_pages, int page_size, int page_shift,
     int64_t seq_stride, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
-    float* __restrict__ scores, int64_t ld, int keys_per_wg, int n_chunks) {
+    float* __restrict__ scores, int64_t ld, int keys_per_wg, int n_chunks,
+    float* __restrict__ samp = nullptr, int samp_min_n = 0) {
   extern __shared__ int spage[];  // paged: physical page of each logical page of this range
   // Block b takes chunk b % n_chunks of row b / n_chunks: consecutive blocks (which the
   // dispatcher deals round-robin to the eight XCDs) walk along a row, so rows of different
@@ -135,7 +142,13 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     const int64_t s_out = s0 + lane;  // the key whose score this lane writes
     const float ks = kscale ? kscale[row_of(min(s_out, wend - 1))] : 1.0f;
     const float tot = trip_scores(qa, wr, kb);
-    if (s_out < wend) srow[s_out] = tot * ks * qs;
+    const float score = tot * ks * qs;
+    if (s_out < wend) srow[s_out] = score;
+    if (SAMPLE && n > samp_min_n && s_out < wend) {
+      // s_out is sample i's position when i = ceil(s_out * kIdxSample / n) maps back to it.
+      const int64_t i = (s_out * kIdxSample + n - 1) / n;
+      if (i < kIdxSample && (i * n) / kIdxSample == s_out) samp[(int64_t)r * kIdxSample + i] = score;
+    }
   }
 }
 
@@ -368,9 +381,9 @@ __global__ __launch_bounds__(256) void index_generic_kernel(
 hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, const float* w,
                                     const CacheView& keys, const int32_t* row_seq,
                                     const int32_t* row_pos, int R, int64_t n_bound, float* scores,
-                                    int64_t ld, hipStream_t s) {
+                                    int64_t ld, hipStream_t s, float* samp, int samp_min_n) {
   const uint8_t* kd = static_cast<const uint8_t*>(keys.data);
-  if (R >= kRowsKernelMin) {
+  if (R >= kRowsKernelMin && !samp) {
     // Many rows: eight rows per workgroup sharing staged key trips; 2048 keys per workgroup.
     const int64_t kpw = 2048;
     const dim3 grid((unsigned)((R + kRowsPerWg - 1) / kRowsPerWg), (unsigned)((n_bound + kpw - 1) / kpw));
@@ -399,13 +412,23 @@ hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, cons
     const int ps = keys.page_size;
     const int shift = (ps & (ps - 1)) == 0 ? __builtin_ctz(ps) : -1;
     const size_t lds = sizeof(int) * (size_t)(kpw / ps + 2);
-    index_fp8_kernel<true><<<grid, kIdxWaves * WAVE, lds, s>>>(
-        q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
-        scores, ld, (int)kpw, n_chunks);
+    if (samp)
+      index_fp8_kernel<true, true><<<grid, kIdxWaves * WAVE, lds, s>>>(
+          q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
+          scores, ld, (int)kpw, n_chunks, samp, samp_min_n);
+    else
+      index_fp8_kernel<true><<<grid, kIdxWaves * WAVE, lds, s>>>(
+          q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
+          scores, ld, (int)kpw, n_chunks);
   } else {
-    index_fp8_kernel<false><<<grid, kIdxWaves * WAVE, 0, s>>>(
-        q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, scores,
-        ld, (int)kpw, n_chunks);
+    if (samp)
+      index_fp8_kernel<false, true><<<grid, kIdxWaves * WAVE, 0, s>>>(
+          q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, scores,
+          ld, (int)kpw, n_chunks, samp, samp_min_n);
+    else
+      index_fp8_kernel<false><<<grid, kIdxWaves * WAVE, 0, s>>>(
+          q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, scores,
+          ld, (int)kpw, n_chunks);
   }
   return hipGetLastError();
 }

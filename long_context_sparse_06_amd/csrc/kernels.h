@@ -16,10 +16,14 @@ struct CacheView {
 };
 
 // ---- indexer
+// samp (optional): rows longer than samp_min_n also store their 2048 evenly spaced sample
+// scores contiguously in samp[R, 2048] (positions (i * n) / 2048); the rows kernel for many
+// rows is not used then.
 hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, const float* w,
                                     const CacheView& keys, const int32_t* row_seq,
                                     const int32_t* row_pos, int R, int64_t n_bound, float* scores,
-                                    int64_t ld, hipStream_t s);
+                                    int64_t ld, hipStream_t s, float* samp = nullptr,
+                                    int samp_min_n = 0);
 hipError_t launch_index_generic(bool fp8, const void* q, const float* q_scale, const float* w,
                                 const CacheView& keys, const int32_t* row_seq, const int32_t* row_pos,
                                 int R, int HI, int dI, int64_t n_bound, float* scores, int64_t ld,
@@ -29,8 +33,13 @@ hipError_t launch_index_generic(bool fp8, const void* q, const float* q_scale, c
 size_t topk_workspace_bytes(int R, int64_t ld, int k);
 // False when R rows of length ld need more blocks than one launch can take.
 bool topk_shape_ok(int R, int64_t ld);
+// samp (optional): each long row's 2048 sample scores, contiguous (see the indexer);
+// the rows' lengths are n_valid[r] + n_off.
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
-                       int32_t* idx, void* ws, hipStream_t s);
+                       int32_t* idx, void* ws, hipStream_t s, const float* samp = nullptr,
+                       int n_off = 0);
+// Rows longer than this use the sampled compaction (and so want the indexer's sample).
+int topk_long_row_min();
 
 // ---- sparse MLA
 size_t mla_decode_workspace_bytes(int B, int H, int Dv, int k);

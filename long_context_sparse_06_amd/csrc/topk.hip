@@ -379,10 +379,12 @@ __device__ void emit_selected(const Src& src, int m, const Threshold& th, SelSta
 // 4096-score chunk are in flight, then compacts the chunk's survivors (key >= theta) in
 // index order into the chunk's slot of the candidate buffer and records their count.
 // Chunk 0 also records theta and the survivor-bin shift for the resolve.
+// With `gsamp` (the fused index + top-k call) the sample comes contiguously from gsamp[r, :],
+// which the indexer filled with the scores at the same positions.  n = n_valid[r] + n_off.
 __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
     RowHeader* __restrict__ hdr, uint32_t* __restrict__ counts, int max_chunks,
-    uint2* __restrict__ cand) {
+    uint2* __restrict__ cand, const float* __restrict__ gsamp, int n_off) {
   __shared__ uint32_t samp[kSample];
   __shared__ __attribute__((aligned(16))) int hist[kPassMax * kHistBins];
   __shared__ SelState st;
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
   // evenly over the XCDs.
   const int r = blockIdx.x / max_chunks;
   const int c = blockIdx.x % max_chunks;
-  int64_t n64 = n_valid[r];
+  int64_t n64 = (int64_t)n_valid[r] + n_off;
   n64 = n64 < 0 ? 0 : (n64 > ld ? ld : n64);
   const int n = (int)n64;
   if (n <= kRowMax || n <= k) return;
@@ -416,7 +418,9 @@ __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
     constexpr int kPer = kSample / kLongThreads;
     uint32_t kv[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) kv[u] = float_key(row[(int64_t)(tid + u * kLongThreads) * n / kSample]);
+    for (int u = 0; u < kPer; ++u)
+      kv[u] = float_key(gsamp ? gsamp[(int64_t)r * kSample + tid + u * kLongThreads]
+                              : row[(int64_t)(tid + u * kLongThreads) * n / kSample]);
     uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -714,14 +718,14 @@ __device__ void resolve_long_row(const float* __restrict__ row, int ld, int n, i
 __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
     int32_t* __restrict__ idx, const RowHeader* __restrict__ hdr, const uint32_t* __restrict__ counts,
-    int max_chunks, const uint2* __restrict__ cand) {
+    int max_chunks, const uint2* __restrict__ cand, int n_off) {
   static_assert(kRowThreads == kResolveThreads, "one kernel serves both paths");
   extern __shared__ uint32_t smem[];  // long rows: survivor keys, ids and chunk offsets
   __shared__ __attribute__((aligned(16))) int hist[kPassMax * kHistBins];
   __shared__ uint2 ties[kTieMax];
   __shared__ SelState st;
   const int r = blockIdx.x;
-  int64_t n64 = n_valid[r];
+  int64_t n64 = (int64_t)n_valid[r] + n_off;
   n64 = n64 < 0 ? 0 : (n64 > ld ? ld : n64);
   const int n = (int)n64;
   int32_t* out = idx + (int64_t)r * k;
@@ -758,6 +762,8 @@ WsLayout ws_layout(int R, int64_t ld) {
 
 }  // namespace
 
+int topk_long_row_min() { return kRowMax; }
+
 bool topk_shape_ok(int R, int64_t ld) {
   return (int64_t)R * ws_layout(1, ld).max_chunks <= 2147483647LL;
 }
@@ -768,7 +774,7 @@ size_t topk_workspace_bytes(int R, int64_t ld, int k) {
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
-                       int32_t* idx, void* ws, hipStream_t s) {
+                       int32_t* idx, void* ws, hipStream_t s, const float* samp, int n_off) {
   const WsLayout L = ws_layout(R, ld);
   char* wsb = static_cast<char*>(ws);
   RowHeader* hdr = L.total ? reinterpret_cast<RowHeader*>(wsb + L.hdr) : nullptr;
@@ -776,14 +782,14 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, 
   uint2* cand = L.total ? reinterpret_cast<uint2*>(wsb + L.cand) : nullptr;
   if (L.total) {
     topk_prep_kernel<<<(unsigned)R * (unsigned)L.max_chunks, kLongThreads, 0, s>>>(
-        scores, ld, n_valid, k, hdr, counts, L.max_chunks, cand);
+        scores, ld, n_valid, k, hdr, counts, L.max_chunks, cand, samp, n_off);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // Long rows: survivor keys and ids, then the chunk offsets (rows up to kRowMax need none).
   const size_t lds = L.total ? sizeof(uint32_t) * (2 * (size_t)kCandCap + L.max_chunks + 1) : 0;
   topk_finish_kernel<<<R, kRowThreads, lds, s>>>(
-      scores, ld, n_valid, k, idx, hdr, counts, L.max_chunks, cand);
+      scores, ld, n_valid, k, idx, hdr, counts, L.max_chunks, cand, n_off);
   return hipGetLastError();
 }
 

@@ -5,12 +5,15 @@ The pages' order -- "FP8 index -> top-k selection -> sparse core attention"
 Attention (DSA) ...") -- run as dsa_index_scores -> dsa_topk -> dsa_sparse_mla_*.
 These classes only own the intermediate buffers (score rows, kept indices,
 workspaces, outputs; allocated once, at construction) and issue the calls in order.
+A decode step runs the first two as the one call dsa_index_topk (same result);
+index() and topk() issue them separately, for per-stage timing.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (BF16, E4M3, F32, Cache, dsa_index_scores, dsa_sparse_mla_decode,
+from . import (BF16, E4M3, F32, Cache, dsa_index_scores, dsa_index_topk,
+               dsa_index_topk_workspace_size, dsa_sparse_mla_decode,
                dsa_sparse_mla_decode_workspace_size, dsa_sparse_mla_prefill, dsa_topk,
                dsa_topk_workspace_size)
 
@@ -36,7 +39,11 @@ class DecodeStep:
         self.kv = Cache(kv, None, block_table, page_size, seq_stride)
         self.idx_dt = F32 if fp32 else E4M3
         self.mla_dt = F32 if fp32 else BF16
-        self.scores = torch.empty(self.B, self.ld, dtype=torch.float32, device=dev)
+        fw = dsa_index_topk_workspace_size(self.B, self.ld, self.k)
+        self.fused_ws = torch.empty(max(fw, 1), dtype=torch.uint8, device=dev)
+        self.fused_ws_bytes = fw
+        # the fused call leaves the scores [B, ld] at the start of its workspace
+        self.scores = self.fused_ws[: self.B * self.ld * 4].view(torch.float32).view(self.B, self.ld)
         self.idx = torch.empty(self.B, self.k, dtype=torch.int32, device=dev)
         tw = dsa_topk_workspace_size(self.B, self.ld, self.k)
         self.topk_ws = torch.empty(max(tw, 1), dtype=torch.uint8, device=dev)
@@ -65,14 +72,18 @@ class DecodeStep:
         dsa_topk(self.scores, self.ld, self.n_valid, self.B, self.k, self.idx, self.topk_ws,
                  self.topk_ws_bytes, stream)
 
+    def index_topk(self, stream=None):
+        dsa_index_topk(self.idx_dt, self.q_idx, self.q_scale, self.w, self.keys, self.row_seq,
+                       self.row_pos, self.B, self.HI, self.dI, self.k, self.idx, self.fused_ws,
+                       self.fused_ws_bytes, stream)
+
     def attend(self, stream=None):
         dsa_sparse_mla_decode(self.mla_dt, self.q, self.kv, self.idx, self.B, self.H, self.Dqk,
                               self.Dv, self.k, self.scale, self.out, self.lse, self.mla_ws,
                               self.mla_ws_bytes, stream)
 
     def run(self, stream=None):
-        self.index(stream)
-        self.topk(stream)
+        self.index_topk(stream)
         self.attend(stream)
         return self.out, self.lse, self.idx
 

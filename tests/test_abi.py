@@ -73,6 +73,14 @@ def test_host_validation_paths():
     assert L.dsa_sparse_mla_decode(dsa.BF16, FAKE, ctypes.byref(kv), FAKE, 8, 128, 576, 512, 2048, 0.04, FAKE, None, FAKE, mw - 1, None) == 4
     assert L.dsa_sparse_mla_prefill(dsa.BF16, FAKE, FAKE, FAKE, 0, 128, 576, 512, 2048, 0.04, FAKE, None, None) == 2
     assert L.dsa_sparse_mla_prefill(dsa.F32, FAKE, FAKE, FAKE, 16, 4, 2000, 64, 32, 0.1, FAKE, None, None) == 6
+    # fused index + top-k
+    fw = L.dsa_index_topk_workspace_size(4, 131072, 2048)
+    assert fw > 4 * 131072 * 4
+    assert L.dsa_index_topk(dsa.E4M3, None, None, FAKE, ctypes.byref(c), FAKE, FAKE, 4, 64, 128, 2048, FAKE, FAKE, fw, None) == 1
+    assert L.dsa_index_topk(dsa.E4M3, FAKE, None, FAKE, ctypes.byref(c), FAKE, FAKE, 4, 64, 128, 0, FAKE, FAKE, fw, None) == 2
+    assert L.dsa_index_topk(dsa.BF16, FAKE, None, FAKE, ctypes.byref(c), FAKE, FAKE, 4, 64, 128, 2048, FAKE, FAKE, fw, None) == 3
+    need = L.dsa_index_topk_workspace_size(4, 1024, 2048)
+    assert L.dsa_index_topk(dsa.E4M3, FAKE, None, FAKE, ctypes.byref(c), FAKE, FAKE, 4, 64, 128, 2048, FAKE, FAKE, need - 1, None) == 4
     # cache append
     ks = dsa._Cache(FAKE, FAKE, None, 0, 0, 1024)
     noscale = dsa._Cache(FAKE, None, None, 0, 0, 1024)

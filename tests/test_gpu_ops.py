@@ -130,6 +130,38 @@ def test_index_scores_generic_fp32():
         parity.check_scores(got[t, : t + 1], ref, ref_abs, f"t={t}")
 
 
+# ----------------------------------------------------------------------------- fused index + top-k
+@pytest.mark.parametrize("paged", [False, True])
+def test_index_topk_equals_the_two_calls(paged):
+    """dsa_index_topk returns exactly dsa_topk(dsa_index_scores(...)) with n_valid = pos + 1:
+    long rows (sampled threshold fed by the indexer's contiguous sample), mid and short rows;
+    two rows are also checked against the oracle's top-k under the band rule."""
+    import long_context_sparse_06_amd as dsa
+    _case(f"index_topk paged={paged}")
+    lengths = np.array([70000, 33000, 40000, 5000, 1500, 2049])
+    inp = datagen.make_decode(len(lengths), None, FULL, seed=51, lengths=lengths, paged=paged)
+    d = upload_decode(inp)
+    B, k = d.B, FULL.k
+    cache = dsa.Cache(d.keys, d.k_scale, d.block_table, d.page_size, d.seq_stride)
+    scores = torch.empty((B, d.ld), device="cuda")
+    dsa.dsa_index_scores(dsa.E4M3, d.q_idx, d.q_scale, d.w, cache, d.row_seq, d.row_pos, B, FULL.HI,
+                         FULL.dI, scores, d.ld)
+    ref_idx = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    tw = dsa.dsa_topk_workspace_size(B, d.ld, k)
+    tws = torch.empty(max(tw, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_topk(scores, d.ld, d.n_valid, B, k, ref_idx, tws, tw)
+    fw = dsa.dsa_index_topk_workspace_size(B, d.ld, k)
+    fws = torch.empty(fw, dtype=torch.uint8, device="cuda")
+    got = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    dsa.dsa_index_topk(dsa.E4M3, d.q_idx, d.q_scale, d.w, cache, d.row_seq, d.row_pos, B, FULL.HI,
+                       FULL.dI, k, got, fws, fw)
+    got_np, ref_np = got.cpu().numpy(), ref_idx.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got_np[b], ref_np[b]), f"row {b} (n={lengths[b]}) differs from the two-call path"
+    for b in (0, 3):
+        parity.check_index_set(got_np[b], pipeline.decode_scores(inp, b), k, f"row {b}")
+
+
 # ----------------------------------------------------------------------------- cache append
 @pytest.mark.parametrize("paged", [False, True])
 def test_cache_append_matches_oracle_quantiser(paged):
