@@ -231,6 +231,26 @@ def main():
     fused_cmp["same_result"] = bool(torch.equal(fidx, st0.idx))
     del fws
 
+    # ---- indexer-quality diagnostic on the same step's scores and kept sets (forward only)
+    qw = dsa.dsa_indexer_quality_workspace_size(B, sh.H, st0.ld)
+    qws = torch.empty(qw, dtype=torch.uint8, device=dev)
+    qkl = torch.empty(B, device=dev)
+    qrc = torch.empty(B, device=dev)
+    qargs = (st0.q, st0.kv, st0.scores, st0.ld, st0.idx, st0.row_seq, st0.row_pos, B, sh.H, sh.Dqk,
+             sh.k, scale, qkl, qrc, qws, qw)
+    dsa.dsa_indexer_quality(*qargs)
+    q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    q0.record(stream)
+    for _ in range(3):
+        dsa.dsa_indexer_quality(*qargs)
+    q1.record(stream)
+    torch.cuda.synchronize()
+    q_us = q0.elapsed_time(q1) * 1e3 / 3
+    q_flops = float(L.sum()) * sh.H * sh.Dqk * 2
+    quality = {"us": q_us, "logit_flops": q_flops, "TFLOP_s": q_flops / (q_us * 1e6),
+               "kl_mean": float(qkl.mean()), "recall_mean": float(qrc.mean())}
+    del qws
+
     # ---- cache append (the step before the indexer): one new token per sequence, written
     # into scratch caches of the same row widths (timed alone; not part of the step above)
     ap_k = torch.randn(B, sh.dI, device=dev) * 0.1
@@ -324,6 +344,7 @@ def main():
                           "index_frac_of_achievable": achieved / copy_gbs},
         "step_us_spread": spread,
         "index_topk_fused_vs_separate": fused_cmp,
+        "indexer_quality": quality,
         "cache_append": {"us": append_us, "alg_bytes": append_bytes,
                          "GB_s": append_bytes / (append_us * 1e3), "bound": "latency"},
         "topk_diagnostic": tie,

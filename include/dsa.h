@@ -14,7 +14,8 @@
  *      dsa_sparse_mla_prefill token per sequence (decode) or every token (prefill)
  *   and, before them, dsa_cache_append: the new token's FP8 indexer key and latent row
  *   written into the caches; dsa_index_topk: steps 1 and 2 in one call;
- *   dsa_masked_mla_prefill: step 3 of a prefill in dense masked form, for short sequences.
+ *   dsa_masked_mla_prefill: step 3 of a prefill in dense masked form, for short sequences;
+ *   dsa_indexer_quality: a forward-only diagnostic of the indexer against dense attention.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned,
@@ -171,6 +172,30 @@ dsa_status dsa_index_topk(dsa_dtype dt, const void* q, const float* q_scale, con
                           const dsa_cache* keys, const int32_t* row_seq, const int32_t* row_pos,
                           int R, int H_I, int d_I, int k, int32_t* idx, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/*
+ * dsa_indexer_quality -- forward-only diagnostic of how well the index scores imitate dense
+ * attention, the quantity the pages say the indexer is trained on (MarkTechPost article
+ * above, "Training signal": the indexer imitates the dense model's head-summed attention
+ * distribution through a KL divergence).  For row r with n = row_pos[r] + 1 candidates:
+ *   p[s]      = (1/H) sum_h softmax_s(softmax_scale * q[r, h, :] . kv[s, :])   (all s < n)
+ *   kl[r]     = sum_s p[s] * (ln p[s] - ln softmax_s(scores[r, s]))   (nats, the dense
+ *               distribution as the target)
+ *   recall[r] = sum of p[s] over the kept set { idx[r, j] : 0 <= idx[r, j] < n }
+ *
+ *   q [R, H, Dqk] bf16     kv  bf16 latent cache, contiguous or paged (as the decode call)
+ *   scores [R, ld] fp32 (as dsa_index_scores wrote them)   idx [R, k] int32 (as dsa_topk)
+ *   kl, recall [R] fp32 outputs
+ *   ws  device workspace of at least dsa_indexer_quality_workspace_size(R, H, ld) bytes (it
+ *       holds every head's logits: R * H * ld fp32)
+ * Limits: H a multiple of 16 and <= 128, Dqk a multiple of 32 and <= 576 (else
+ * DSA_ERR_UNSUPPORTED); ld >= the cache's capacity.
+ */
+size_t dsa_indexer_quality_workspace_size(int R, int H, int64_t ld);
+dsa_status dsa_indexer_quality(const void* q, const dsa_cache* kv, const float* scores, int64_t ld,
+                               const int32_t* idx, const int32_t* row_seq, const int32_t* row_pos,
+                               int R, int H, int Dqk, int k, float softmax_scale, float* kl,
+                               float* recall, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * dsa_masked_mla_prefill -- the same result as dsa_sparse_mla_prefill, computed in the

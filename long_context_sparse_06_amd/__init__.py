@@ -18,7 +18,8 @@ __all__ = [
     "DSAError", "DSALibraryMissing", "Cache", "F32", "BF16", "E4M3", "LIB_PATH", "lib",
     "dsa_index_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_decode",
     "dsa_sparse_mla_decode_workspace_size", "dsa_sparse_mla_prefill", "dsa_masked_mla_prefill",
-    "dsa_index_topk", "dsa_index_topk_workspace_size",
+    "dsa_index_topk", "dsa_index_topk_workspace_size", "dsa_indexer_quality",
+    "dsa_indexer_quality_workspace_size",
     "dsa_cache_append",
     "dsa_status_string", "exported_symbols",
 ]
@@ -62,6 +63,9 @@ _SIGS = {
     "dsa_index_topk_workspace_size": (_sz, [_i32, _i64, _i32]),
     "dsa_index_topk": (_i32, [_i32, _vp, _vp, _vp, ctypes.POINTER(_Cache), _vp, _vp, _i32, _i32, _i32,
                               _i32, _vp, _vp, _sz, _vp]),
+    "dsa_indexer_quality_workspace_size": (_sz, [_i32, _i32, _i64]),
+    "dsa_indexer_quality": (_i32, [_vp, ctypes.POINTER(_Cache), _vp, _i64, _vp, _vp, _vp, _i32, _i32,
+                                   _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "dsa_masked_mla_prefill": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp]),
     "dsa_cache_append": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, ctypes.POINTER(_Cache),
@@ -207,4 +211,21 @@ def dsa_index_topk(dt: int, q, q_scale, w, keys: Cache, row_seq, row_pos, R: int
     _check("dsa_index_topk", lib().dsa_index_topk(
         dt, _ptr(q), _ptr(q_scale), _ptr(w), ctypes.byref(c), _ptr(row_seq), _ptr(row_pos), R, H_I,
         d_I, k, _ptr(idx), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dsa_indexer_quality_workspace_size(R: int, H: int, ld: int) -> int:
+    return int(lib().dsa_indexer_quality_workspace_size(R, H, ld))
+
+
+def dsa_indexer_quality(q, kv: Cache, scores, ld: int, idx, row_seq, row_pos, R: int, H: int,
+                        Dqk: int, k: int, softmax_scale: float, kl, recall, ws, ws_bytes: int = 0,
+                        stream=None):
+    """Per row: KL(dense head-averaged attention || softmax(index scores)) and the kept set's
+    dense attention mass."""
+    if ws is not None and not ws_bytes:
+        ws_bytes = ws.numel() * ws.element_size()
+    c = kv._c()
+    _check("dsa_indexer_quality", lib().dsa_indexer_quality(
+        _ptr(q), ctypes.byref(c), _ptr(scores), ld, _ptr(idx), _ptr(row_seq), _ptr(row_pos), R, H,
+        Dqk, k, softmax_scale, _ptr(kl), _ptr(recall), _ptr(ws), ws_bytes, _stream(stream)))
 

@@ -179,6 +179,28 @@ dsa_status dsa_index_topk(dsa_dtype dt, const void* q, const float* q_scale, con
   return launched(dsa::launch_topk(scores, cap, row_pos, R, k, idx, tws, stream, nullptr, 1));
 }
 
+size_t dsa_indexer_quality_workspace_size(int R, int H, int64_t ld) {
+  if (R <= 0 || H <= 0 || ld <= 0) return 0;
+  return dsa::quality_workspace_bytes(R, H, ld);
+}
+
+dsa_status dsa_indexer_quality(const void* q, const dsa_cache* kv, const float* scores, int64_t ld,
+                               const int32_t* idx, const int32_t* row_seq, const int32_t* row_pos,
+                               int R, int H, int Dqk, int k, float softmax_scale, float* kl,
+                               float* recall, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !kv || !kv->data || !scores || !idx || !row_seq || !row_pos || !kl || !recall)
+    return DSA_ERR_NULL;
+  if (R <= 0 || H <= 0 || Dqk <= 0 || k <= 0 || ld <= 0 || R > 65535) return DSA_ERR_SHAPE;
+  const int64_t cap = cache_capacity(kv);
+  if (cap <= 0 || ld < cap) return DSA_ERR_SHAPE;
+  if (H % 16 != 0 || H > 128 || Dqk % 32 != 0 || Dqk > 576) return DSA_ERR_UNSUPPORTED;
+  if ((int64_t)R * ((ld + 63) / 64) > 2147483647LL) return DSA_ERR_SHAPE;
+  if (!ws || ws_bytes < dsa::quality_workspace_bytes(R, H, ld)) return DSA_ERR_WORKSPACE;
+  return launched(dsa::launch_indexer_quality(static_cast<const uint16_t*>(q), view(kv), scores, ld, idx, k,
+                                              row_seq, row_pos, R, H, Dqk, ld, softmax_scale, kl, recall,
+                                              ws, stream));
+}
+
 dsa_status dsa_masked_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,
                                   int T, int H, int Dqk, int Dv, int k, float softmax_scale, void* out,
                                   float* lse, hipStream_t stream) {

@@ -58,4 +58,11 @@ hipError_t launch_cache_append(const float* k_new, const uint16_t* kv_new, const
                                const int32_t* row_pos, int R, int dI, int Dqk, const CacheView& keys,
                                const CacheView& kv, hipStream_t s);
 
+// ---- indexer-quality diagnostic
+size_t quality_workspace_bytes(int R, int H, int64_t ld);
+hipError_t launch_indexer_quality(const uint16_t* q, const CacheView& kv, const float* scores,
+                                  int64_t sld, const int32_t* idx, int k, const int32_t* row_seq,
+                                  const int32_t* row_pos, int R, int H, int Dqk, int64_t ld,
+                                  float scale, float* kl, float* recall, void* ws, hipStream_t s);
+
 }  // namespace dsa

@@ -178,3 +178,38 @@ def quantize_key(x: np.ndarray):
     y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     return encode_e4m3(y), scale
 
+
+# ----------------------------------------------------------------------------
+# indexer-quality diagnostic ([MTP] "Training signal": the indexer imitates the dense
+# model's head-summed attention distribution through a KL divergence)
+# ----------------------------------------------------------------------------
+def dense_attention_distribution(q: np.ndarray, kv_rows: np.ndarray, scale: float) -> np.ndarray:
+    """Head-summed dense attention over n candidate rows, normalised to a distribution.
+
+    q [H, Dqk], kv_rows [n, Dqk] -> p [n] = (1/H) sum_h softmax_s(scale * q_h . row_s).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kv_rows = np.asarray(kv_rows, dtype=np.float64)
+    z = scale * (q @ kv_rows.T)                     # [H, n]
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=1, keepdims=True)).mean(axis=0)
+
+
+def indexer_quality(p_attn: np.ndarray, scores: np.ndarray, kept) -> tuple:
+    """(KL(p_attn || softmax(scores)), attention mass of the kept set) for one query row.
+
+    p_attn [n] the dense distribution (the imitation target), scores [n] the index scores,
+    kept the selected positions.  KL in nats; terms with p_attn = 0 contribute 0.
+    """
+    p = np.asarray(p_attn, dtype=np.float64)
+    i = np.asarray(scores, dtype=np.float64)
+    log_q = i - i.max()
+    log_q = log_q - np.log(np.exp(log_q).sum())
+    nz = p > 0
+    kl = float(np.sum(p[nz] * (np.log(p[nz]) - log_q[nz])))
+    kept = np.asarray(kept, dtype=np.int64)
+    kept = kept[kept >= 0]
+    recall = float(p[kept].sum())
+    return kl, recall
+

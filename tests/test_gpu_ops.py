@@ -162,6 +162,43 @@ def test_index_topk_equals_the_two_calls(paged):
         parity.check_index_set(got_np[b], pipeline.decode_scores(inp, b), k, f"row {b}")
 
 
+# ----------------------------------------------------------------------------- indexer quality
+@pytest.mark.parametrize("paged,regime", [(False, "peaked"), (True, "gaussian")])
+def test_indexer_quality_matches_oracle(paged, regime):
+    """KL(dense head-averaged attention || softmax(scores)) and the kept set's attention mass
+    per row, against the oracle fed the same scores and kept sets the GPU produced."""
+    import long_context_sparse_06_amd as dsa
+    _case(f"indexer_quality paged={paged} {regime}")
+    lengths = np.array([5000, 2049, 300, 12000])
+    inp = datagen.make_decode(len(lengths), None, FULL, seed=71, lengths=lengths, paged=paged, regime=regime)
+    d = upload_decode(inp)
+    B, k = d.B, FULL.k
+    cache_k = dsa.Cache(d.keys, d.k_scale, d.block_table, d.page_size, d.seq_stride)
+    cache_v = dsa.Cache(d.kv, None, d.block_table, d.page_size, d.seq_stride)
+    scores = torch.empty((B, d.ld), device="cuda")
+    dsa.dsa_index_scores(dsa.E4M3, d.q_idx, d.q_scale, d.w, cache_k, d.row_seq, d.row_pos, B, FULL.HI,
+                         FULL.dI, scores, d.ld)
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    tw = dsa.dsa_topk_workspace_size(B, d.ld, k)
+    dsa.dsa_topk(scores, d.ld, d.n_valid, B, k, idx, torch.empty(max(tw, 1), dtype=torch.uint8, device="cuda"), tw)
+    scale = 1.0 / math.sqrt(FULL.Dqk)
+    qw = dsa.dsa_indexer_quality_workspace_size(B, FULL.H, d.ld)
+    ws = torch.empty(qw, dtype=torch.uint8, device="cuda")
+    kl = torch.full((B,), float("nan"), device="cuda")
+    rc = torch.full((B,), float("nan"), device="cuda")
+    dsa.dsa_indexer_quality(d.q, cache_v, scores, d.ld, idx, d.row_seq, d.row_pos, B, FULL.H, FULL.Dqk,
+                            k, scale, kl, rc, ws, qw)
+    kl_g, rc_g = kl.cpu().numpy(), rc.cpu().numpy()
+    s_np, i_np = scores.cpu().numpy(), idx.cpu().numpy()
+    for b in range(B):
+        L = int(lengths[b])
+        kl_r, rc_r = pipeline.decode_indexer_quality(inp, b, scale, i_np[b], scores=s_np[b, :L])
+        print(f"  row {b}: kl {kl_g[b]:.6f} / {kl_r:.6f}  recall {rc_g[b]:.6f} / {rc_r:.6f}", flush=True)
+        assert abs(kl_g[b] - kl_r) <= 1e-4 * abs(kl_r) + 2e-5, f"row {b}: kl {kl_g[b]} vs {kl_r}"
+        assert abs(rc_g[b] - rc_r) <= 1e-4 * rc_r + 1e-6, f"row {b}: recall {rc_g[b]} vs {rc_r}"
+    assert abs(rc_g[2] - 1.0) < 1e-5          # n = 300 <= k: every candidate is kept
+
+
 # ----------------------------------------------------------------------------- cache append
 @pytest.mark.parametrize("paged", [False, True])
 def test_cache_append_matches_oracle_quantiser(paged):

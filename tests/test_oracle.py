@@ -344,3 +344,37 @@ def test_decode_row_equals_last_prefill_row():
         q_idx = pre.q_idx[39:40]; q_scale = pre.q_scale[39:40]; w = pre.w[39:40]
         keys = pre.keys[None]; k_scale = pre.k_scale[None]; q = pre.q[39:40]; kv = pre.kv[None]
     np.testing.assert_array_equal(pipeline.decode_scores(D, 0), s_pre)
+
+
+# ----------------------------------------------------------------------------- indexer quality
+def test_dense_attention_distribution_matches_scipy_softmax_mean():
+    from scipy.special import softmax
+    rng = np.random.default_rng(61)
+    q = rng.standard_normal((5, 12))
+    rows = rng.standard_normal((30, 12))
+    ref = softmax(0.3 * (q @ rows.T), axis=1).mean(axis=0)
+    got = oracle.dense_attention_distribution(q, rows, 0.3)
+    assert np.allclose(got, ref, rtol=1e-13, atol=0) and abs(got.sum() - 1) < 1e-13
+    # zero queries attend uniformly
+    assert np.allclose(oracle.dense_attention_distribution(np.zeros((3, 12)), rows, 0.3), 1 / 30)
+
+
+def test_indexer_quality_closed_forms_and_scipy_entropy():
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    rng = np.random.default_rng(62)
+    p = softmax(rng.standard_normal(40))
+    s = rng.standard_normal(40) * 3
+    kl, rec = oracle.indexer_quality(p, s, np.arange(40))
+    assert abs(kl - entropy(p, softmax(s))) < 1e-12
+    assert abs(rec - 1.0) < 1e-12 and kl >= 0
+    kl0, _ = oracle.indexer_quality(p, np.log(p) + 7.0, [])
+    assert abs(kl0) < 1e-12                                   # scores = log target (+ const)
+    kl_u, rec_u = oracle.indexer_quality(np.full(8, 1 / 8), np.zeros(8), [1, 3, -1])
+    assert abs(kl_u) < 1e-15 and abs(rec_u - 0.25) < 1e-15   # uniform: mass 2/8
+    # one head, two rows, worked by hand: z = (0, ln 3) -> p = (1/4, 3/4); scores (0, 0)
+    p2 = oracle.dense_attention_distribution(np.array([[1.0]]), np.array([[0.0], [np.log(3)]]), 1.0)
+    assert np.allclose(p2, [0.25, 0.75], atol=1e-15)
+    kl2, rec2 = oracle.indexer_quality(p2, np.zeros(2), [1])
+    assert abs(kl2 - (0.25 * np.log(0.5) + 0.75 * np.log(1.5))) < 1e-15 and abs(rec2 - 0.75) < 1e-15
+
