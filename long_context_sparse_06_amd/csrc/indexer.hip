@@ -145,9 +145,15 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     const float score = tot * ks * qs;
     if (s_out < wend) srow[s_out] = score;
     if (SAMPLE && n > samp_min_n && s_out < wend) {
-      // s_out is sample i's position when i = ceil(s_out * kIdxSample / n) maps back to it.
-      const int64_t i = (s_out * kIdxSample + n - 1) / n;
-      if (i < kIdxSample && (i * n) / kIdxSample == s_out) samp[(int64_t)r * kIdxSample + i] = score;
+      // s_out is sample i's position when (i * n) / kIdxSample == s_out, i.e. for
+      // i = ceil(s_out * kIdxSample / n); a float estimate of s_out * kIdxSample / n (error far
+      // below 1) leaves that i at its floor or one above, both checked exactly.
+      const int64_t ie = (int64_t)((float)s_out * ((float)kIdxSample / (float)n));
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int64_t i = ie + d;
+        if (i < kIdxSample && (i * n) / kIdxSample == s_out) samp[(int64_t)r * kIdxSample + i] = score;
+      }
     }
   }
 }
