@@ -11,10 +11,14 @@ pass that issues the three calls separately.  The default workload is
 batch 8 x 131072 context (128 query heads, 576-wide bf16 latent rows, 64 x 128 e4m3
 indexer), synthetic N(0,1)/sqrt(d) data (seed 1003).  Inputs are resident in HBM before
 timing starts; `--copies` distinct copies of the caches are rotated step by step so the
-256 MB Infinity Cache cannot serve a step from the previous one.  The step is captured
-once per copy in a HIP graph and replayed (the library never allocates or synchronises,
-so capture is plain); an eager pass of the same steps with HIP events around every
-indexer launch gives the indexer's average duration for the roofline figure.
+256 MB Infinity Cache cannot serve a step from the previous one.  One HIP graph holds a
+step on every copy in turn (as a decode loop captures several attention layers in one
+graph) and is replayed; the library never allocates or synchronises, so capture is plain.
+The same steps replayed one graph per step are reported beside it
+(`single_step_graph_us`: each graph launch adds a gap of several microseconds).  A graph of
+back-to-back indexer launches over the copies, with HIP events around its replays, gives
+the indexer's launch duration for the roofline figure; an eager pass with events around
+each call gives the per-stage breakdown (host gaps included).
 
 `--mode prefill` times one causal prefill of T = 32768 tokens (workload 4) instead and reports
 the indexer (A2) against the FP8 MFMA peak and the sparse MLA (A6) against the bf16 MFMA peak,
@@ -101,9 +105,12 @@ def main():
     roof_us = step_bytes / (HBM_PEAK_GBS * 1e3)
 
     stream = torch.cuda.current_stream()
-    # ---- graphs (one per copy)
+    # ---- graphs: one per copy (a single step), and one holding a step on every copy in
+    # turn, as a decode loop would capture several attention layers in one graph -- launching
+    # a graph per step leaves a gap of several microseconds between graphs
     use_graph = not args.no_graph
     graphs = []
+    multi = None
     if use_graph:
         for st in steps:  # warm the kernels once before capture
             st.run()
@@ -113,6 +120,10 @@ def main():
             with torch.cuda.graph(g):
                 st.run()
             graphs.append(g)
+        multi = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(multi):
+            for st in steps:
+                st.run()
         torch.cuda.synchronize()
 
     def one(i):
@@ -121,15 +132,36 @@ def main():
         else:
             steps[i % len(steps)].run()
 
-    for i in range(args.warmup):
-        one(i)
+    def run_steps(n):
+        # n whole steps, in copy order: full rounds through the multi-step graph, then singles
+        if not use_graph:
+            for i in range(n):
+                one(i)
+            return
+        for _ in range(n // len(steps)):
+            multi.replay()
+        for i in range(n % len(steps)):
+            one(i)
+
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        one(i)
+    run_steps(args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # ---- the same steps replayed one graph per step (reported beside the headline)
+    single_us = None
+    if use_graph:
+        for i in range(len(steps)):
+            one(i)
+        torch.cuda.synchronize()
+        ts0 = time.perf_counter()
+        for i in range(args.steps):
+            one(i)
+        torch.cuda.synchronize()
+        single_us = (time.perf_counter() - ts0) * 1e6 / args.steps
 
     # ---- per-step spread: HIP events around single replays (outside the wall-clock loop)
     spread = None
@@ -167,15 +199,36 @@ def main():
     t_topk = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
     t_mla = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
     idx_us = float(t_idx.mean())
+    if use_graph:
+        # the indexer's launch duration without host gaps: a graph of back-to-back indexer
+        # launches, one per cache copy in turn (caches as cold as in the step), HIP events
+        # around its replays on this stream
+        gi = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gi):
+            for st in steps:
+                st.index()
+        gi.replay()
+        torch.cuda.synchronize()
+        n_rep = max(5, args.steps // len(steps))
+        ia, ib = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ia.record(stream)
+        for _ in range(n_rep):
+            gi.replay()
+        ib.record(stream)
+        torch.cuda.synchronize()
+        idx_us = ia.elapsed_time(ib) * 1e3 / (n_rep * len(steps))
+        del gi
     achieved = idx_bytes / (idx_us * 1e3)  # GB/s
 
     # ---- quick self-check of the timed path against the first copy's eager result
     ok = True
     if use_graph:
         ref = [t.clone() for t in (steps[0].idx, steps[0].out)]
-        graphs[0].replay()
-        torch.cuda.synchronize()
-        ok = torch.equal(ref[0], steps[0].idx) and torch.equal(ref[1].view(torch.int16), steps[0].out.view(torch.int16))
+        for g in (graphs[0], multi):
+            g.replay()
+            torch.cuda.synchronize()
+            ok = ok and torch.equal(ref[0], steps[0].idx) and torch.equal(ref[1].view(torch.int16),
+                                                                          steps[0].out.view(torch.int16))
 
     # ---- top-k on a tie storm (every score equal) beside the same call on the step's scores
     st0 = steps[0]
@@ -204,32 +257,29 @@ def main():
     copy_gbs = 5 * 2 * (1 << 30) / (ca.elapsed_time(cb) * 1e6)
     del src_b, dst_b
 
-    # ---- the fused index + top-k call beside the two separate calls (eager, events)
+    # ---- the fused index + top-k call beside the two separate calls: each as a graph of one
+    # call per cache copy in turn (cold caches, no host gaps), HIP events around replays
     st0 = steps[0]
-    fw = dsa.dsa_index_topk_workspace_size(B, st0.ld, st0.k)
-    fws = torch.empty(fw, dtype=torch.uint8, device=dev)
-    fidx = torch.empty_like(st0.idx)
-
-    def fused():
-        dsa.dsa_index_topk(st0.idx_dt, st0.q_idx, st0.q_scale, st0.w, st0.keys, st0.row_seq,
-                           st0.row_pos, B, st0.HI, st0.dI, st0.k, fidx, fws, fw)
-
-    def separate():
-        st0.index()
-        st0.topk()
-
     fused_cmp = {}
-    for name, fn in (("fused_us", fused), ("separate_us", separate)):
-        fn()
-        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-        for a, b in fe:
-            a.record(stream)
-            fn()
-            b.record(stream)
+    outs = {}
+    for name, fn in (("fused_us", lambda st: st.index_topk()),
+                     ("separate_us", lambda st: (st.index(), st.topk()))):
+        gf = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gf):
+            for st in steps:
+                fn(st)
+        gf.replay()
         torch.cuda.synchronize()
-        fused_cmp[name] = float(np.mean([a.elapsed_time(b) for a, b in fe[2:]]) * 1e3)
-    fused_cmp["same_result"] = bool(torch.equal(fidx, st0.idx))
-    del fws
+        outs[name] = st0.idx.clone()
+        fa, fb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fa.record(stream)
+        for _ in range(10):
+            gf.replay()
+        fb.record(stream)
+        torch.cuda.synchronize()
+        fused_cmp[name] = fa.elapsed_time(fb) * 1e3 / (10 * len(steps))
+        del gf
+    fused_cmp["same_result"] = bool(torch.equal(outs["fused_us"], outs["separate_us"]))
 
     # ---- indexer-quality diagnostic on the same step's scores and kept sets (forward only)
     qw = dsa.dsa_indexer_quality_workspace_size(B, sh.H, st0.ld)
@@ -305,15 +355,17 @@ def main():
     # HBM traffic of the indexer from the committed rocprofv3 counter record; null when the
     # kernel source has changed since the counters were taken.
     traffic = None
+    traffic_detail = None
     try:
         import hashlib
         rec = json.load(open(os.path.join(ROOT, "profiles", f"index_fp8_kernel_{cfg['name']}.traffic.json")))
         src = open(os.path.join(ROOT, rec["source"]), "rb").read()
         if hashlib.sha256(src).hexdigest() == rec["source_sha256"]:
-            traffic = {"fetch_bytes": rec["fetch_bytes"], "write_bytes": rec["write_bytes"],
-                       "GB_per_launch": (rec["fetch_bytes"] + rec["write_bytes"]) / 1e9}
+            traffic = rec["fetch_bytes"] + rec["write_bytes"]  # HBM bytes per launch
+            traffic_detail = {"fetch_bytes": rec["fetch_bytes"], "write_bytes": rec["write_bytes"],
+                              "instance": rec.get("instance"), "vs_alg": traffic / idx_bytes}
     except (OSError, KeyError, ValueError):
-        traffic = None
+        traffic = traffic_detail = None
 
     out = {
         "metric": METRIC,
@@ -333,10 +385,12 @@ def main():
                    "context_mean": float(L.mean()), "top_k": sh.k, "heads": sh.H,
                    "latent": sh.Dqk, "value_dim": sh.Dv, "indexer_heads": sh.HI, "indexer_dim": sh.dI,
                    "paged": inp.block_table is not None, "cache_copies": len(steps),
-                   "graph": use_graph, "parallelism": "single-gpu"},
+                   "graph": use_graph, "steps_per_graph": len(steps) if use_graph else 0,
+                   "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "index_fp8_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "alg_bytes_per_launch": idx_bytes},
+                     "traffic": traffic, "traffic_detail": traffic_detail,
+                     "alg_bytes_per_launch": idx_bytes, "launch_us": idx_us},
         "step_roofline": {"alg_bytes": step_bytes, "roof_us": roof_us,
                           "frac": roof_us / (ms_per_step * 1e3),
                           "achievable_copy_GBs": copy_gbs,
@@ -348,7 +402,8 @@ def main():
         "cache_append": {"us": append_us, "alg_bytes": append_bytes,
                          "GB_s": append_bytes / (append_us * 1e3), "bound": "latency"},
         "topk_diagnostic": tie,
-        "breakdown_us": {"index": idx_us, "topk": float(t_topk.mean()), "sparse_mla": float(t_mla.mean()),
+        "single_step_graph_us": single_us,
+        "breakdown_us": {"index": float(t_idx.mean()), "topk": float(t_topk.mean()), "sparse_mla": float(t_mla.mean()),
                          "eager_step": (te1 - te0) * 1e6 / args.steps},
         "graph_replay_matches_eager": bool(ok),
         "cpu_baseline": cpu,
