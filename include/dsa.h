@@ -132,6 +132,10 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int
  *   out    [B, H, Dv]      lse [B, H] fp32 or NULL
  *   ws     device workspace of at least dsa_sparse_mla_decode_workspace_size(...) bytes
  *          (split-KV partials); may be NULL when that size is 0
+ * Limits: B * H <= 2^31 - 1; off the bf16 fast path (DSA_F32 or other shapes) the
+ * generic kernel needs (Dqk + k + 8) * 4 <= 65536 bytes and Dqk <= 1024, else
+ * DSA_ERR_UNSUPPORTED.  The fast path takes any k (a workgroup holds at most 8192 kept
+ * tokens; longer sets are split further).
  */
 size_t dsa_sparse_mla_decode_workspace_size(int B, int H, int Dv, int k);
 dsa_status dsa_sparse_mla_decode(dsa_dtype dt, const void* q, const dsa_cache* kv,
@@ -146,7 +150,8 @@ dsa_status dsa_sparse_mla_decode(dsa_dtype dt, const void* q, const dsa_cache* k
  *
  *   q [T, H, Dqk]   kv [T, Dqk] (contiguous latent rows of the sequence)   idx [T, k]
  *   out [T, H, Dv]  lse [T, H] fp32 or NULL
- * dt and shape rules as for dsa_sparse_mla_decode.
+ * dt and shape rules as for dsa_sparse_mla_decode.  Limits: as there, and k <= 8192 on the
+ * bf16 fast path (one workgroup holds a row's whole kept set; else DSA_ERR_UNSUPPORTED).
  */
 dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,
                                   int T, int H, int Dqk, int Dv, int k, float softmax_scale,
@@ -206,7 +211,8 @@ dsa_status dsa_indexer_quality(const void* q, const dsa_cache* kv, const float* 
  * No row gather, but the cost grows with t rather than |S_t|: it pays while t + 1 is
  * within a small multiple of k.
  *
- *   arguments, layouts, dtypes and limits as dsa_sparse_mla_prefill; T <= 65536.
+ *   arguments, layouts and dtypes as dsa_sparse_mla_prefill; T <= 65536, any k on the bf16
+ *   fast path (the kept set only sets mask bits), the generic kernel's limit otherwise.
  * Shapes off the bf16 fast path are served by the same generic kernel as the sparse call.
  */
 dsa_status dsa_masked_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,

@@ -120,10 +120,12 @@ dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, c
   dsa_status st = mla_check(dt, q, kv, idx, T, H, Dqk, Dv, k, out);
   if (st != DSA_OK) return st;
   const dsa::CacheView v{kv, nullptr, nullptr, 0, 0, (int64_t)T};
-  if (mla_fast(dt, H, Dqk, Dv))
+  if (mla_fast(dt, H, Dqk, Dv)) {
+    if (k > dsa::mla_max_tokens_per_wg()) return DSA_ERR_UNSUPPORTED;
     return launched(dsa::launch_mla_bf16(static_cast<const uint16_t*>(q), v, idx, T, H, k, false,
                                          softmax_scale, static_cast<uint16_t*>(out), lse, nullptr, 0,
                                          stream));
+  }
   if ((st = mla_generic_ok(Dqk, k)) != DSA_OK) return st;
   return launched(dsa::launch_mla_generic(dt == DSA_BF16, q, v, idx, T, H, Dqk, Dv, k, false,
                                           softmax_scale, out, lse, stream));

@@ -43,6 +43,7 @@ int topk_long_row_min();
 
 // ---- sparse MLA
 size_t mla_decode_workspace_bytes(int B, int H, int Dv, int k);
+int mla_max_tokens_per_wg();  // longest kept set one bf16 workgroup holds (prefill: k limit)
 hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t* idx, int R,
                            int H, int k, bool decode, float scale, uint16_t* out, float* lse,
                            void* ws, size_t ws_bytes, hipStream_t s);

@@ -564,10 +564,14 @@ __global__ __launch_bounds__(256) void mla_generic_kernel(
   if (lse && tid == 0) lse[(int64_t)r * H + h] = L > 0.0f ? M + logf(L) : -INFINITY;
 }
 
-// Dynamic LDS of the bf16 kernel: the row list and one live-token mask per tile.
+// Dynamic LDS of the bf16 kernel: the row list and one live-token mask per tile.  The
+// static part (ring, logit exchange) takes 124 KB of the 160 KB, which leaves room for the
+// list of kMaxTokPerWg tokens.
 size_t mla_lds_bytes(int tok_per_split) {
   return sizeof(int) * ((size_t)tok_per_split + (tok_per_split + kTok - 1) / kTok);
 }
+
+constexpr int kMaxTokPerWg = 8192;  // kept tokens one workgroup of the bf16 kernel can hold
 
 struct SplitPlan {
   int n_split, tok_per_split;
@@ -575,11 +579,14 @@ struct SplitPlan {
 
 SplitPlan split_plan(int B, int H, int k) {
   // One workgroup per CU (the LDS ring allows no second one): split each sequence's kept
-  // set until ~256 workgroups exist, keeping at least 4 tiles (128 rows) per workgroup.
+  // set until ~256 workgroups exist, keeping at least 4 tiles (128 rows) per workgroup and
+  // at most kMaxTokPerWg tokens (the row list sits in LDS beside the ring).
   const int groups = B * (H / kHeadsPerWg);
   int ns = (256 + groups - 1) / groups;
   const int max_ns = (k + 4 * kTok - 1) / (4 * kTok);
   ns = ns < 1 ? 1 : (ns > max_ns ? max_ns : ns);
+  const int min_ns = (k + kMaxTokPerWg - 1) / kMaxTokPerWg;
+  ns = ns < min_ns ? min_ns : ns;
   int tps = (k + ns - 1) / ns;
   tps = (tps + kTok - 1) / kTok * kTok;
   ns = (k + tps - 1) / tps;
@@ -587,6 +594,8 @@ SplitPlan split_plan(int B, int H, int k) {
 }
 
 }  // namespace
+
+int mla_max_tokens_per_wg() { return kMaxTokPerWg; }
 
 size_t mla_decode_workspace_bytes(int B, int H, int Dv, int k) {
   if (Dv != kDv || H % kHeadsPerWg != 0) return 0;  // generic path needs no workspace

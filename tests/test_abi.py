@@ -73,6 +73,18 @@ def test_host_validation_paths():
     assert L.dsa_sparse_mla_decode(dsa.BF16, FAKE, ctypes.byref(kv), FAKE, 8, 128, 576, 512, 2048, 0.04, FAKE, None, FAKE, mw - 1, None) == 4
     assert L.dsa_sparse_mla_prefill(dsa.BF16, FAKE, FAKE, FAKE, 0, 128, 576, 512, 2048, 0.04, FAKE, None, None) == 2
     assert L.dsa_sparse_mla_prefill(dsa.F32, FAKE, FAKE, FAKE, 16, 4, 2000, 64, 32, 0.1, FAKE, None, None) == 6
+    # a prefill row's whole kept set sits in one bf16 workgroup: k <= 8192
+    assert L.dsa_sparse_mla_prefill(dsa.BF16, FAKE, FAKE, FAKE, 16, 128, 576, 512, 8193, 0.04, FAKE, None, None) == 6
+    # generic kernel: logits of one (row, head) plus the query row in 64 KB of LDS
+    assert L.dsa_sparse_mla_decode(dsa.F32, FAKE, ctypes.byref(kv), FAKE, 8, 128, 576, 512, 16000, 0.04, FAKE, None, None, 0, None) == 6
+    # split plan, read back from the workspace size (B * splits * H partial rows of 512 bf16
+    # values + (max, sum)): ~256 workgroups at batch 8; no workgroup holds more than 8192
+    # kept tokens even when the batch alone fills the GPU
+    part = 512 * 2 + 8
+    assert mw == 8 * 16 * 128 * part
+    assert L.dsa_sparse_mla_decode_workspace_size(128, 128, 512, 2048) == 0       # one split
+    assert L.dsa_sparse_mla_decode_workspace_size(128, 128, 512, 16384) == 128 * 2 * 128 * part
+    assert L.dsa_sparse_mla_decode_workspace_size(512, 128, 512, 9000) == 512 * 2 * 128 * part
     # fused index + top-k
     fw = L.dsa_index_topk_workspace_size(4, 131072, 2048)
     assert fw > 4 * 131072 * 4

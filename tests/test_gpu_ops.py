@@ -383,6 +383,33 @@ def test_topk_long_rows_boundary_bin():
     _expect_topk(s[5:], [ld], 100, got)
 
 
+def test_topk_largest_k():
+    """k = 16384 (the largest accepted): long rows (sampled threshold; more survivors are needed
+    than the survivor list holds, so the full-row select runs), register-resident mid rows,
+    n = k, n < k, and a coarse row with a big tie at the threshold."""
+    _case("topk k = 16384")
+    rng = np.random.default_rng(36)
+    ld, k = 131072, 16384
+    n_valid = [131072, 32768, 20000, 16384, 9000, 131072]
+    s = rng.standard_normal((len(n_valid), ld)).astype(np.float32)
+    s[5] = np.round(s[5] * 4) / 4
+    got = _run_topk(s, n_valid, k)
+    _expect_topk(s, n_valid, k, got)
+
+
+def test_topk_longest_row():
+    """Rows of the largest accepted length, ld = 2^24 (64 MB of scores each), one full and
+    one ragged, with a planted block of large scores and ties among them."""
+    _case("topk ld = 2^24")
+    rng = np.random.default_rng(37)
+    ld, k = 1 << 24, 2048
+    s = rng.standard_normal((2, ld)).astype(np.float32)
+    s[1, 5_000_000:5_001_500] = np.round(rng.uniform(4, 5, 1500) * 16) / 16
+    n_valid = [ld, ld - 12345]
+    got = _run_topk(s, n_valid, k)
+    _expect_topk(s, n_valid, k, got)
+
+
 # ----------------------------------------------------------------------------- sparse MLA
 def _random_sets(rng, lengths, k, holes=True):
     B = len(lengths)
@@ -419,6 +446,86 @@ def test_sparse_mla_decode_bf16(paged, regime):
         parity.check_attention(o[b], l[b], o_ref, lse_ref, parity.BF16_ATOL, f"b={b}")
         if regime == "peaked":
             assert parity.rel_l2(o[b], o_ref) <= 1e-2
+
+
+def test_sparse_mla_decode_largest_sets():
+    """Kept sets beyond the 2048 of the workloads: k = 16384 at batch 2 (many splits), and a
+    batch of 128 sequences (enough workgroups without splitting) with k = 9000, where each
+    workgroup may hold at most 8192 kept tokens so the set is still split in two.  The 128
+    sequences share one paged pool through their block tables (pages may be shared)."""
+    import long_context_sparse_06_amd as dsa
+    from oracle import sparse_mla
+    scale = 1.0 / math.sqrt(FULL.Dqk)
+
+    _case("sparse_mla_decode k = 16384, batch 2")
+    rng = np.random.default_rng(47)
+    lengths = np.array([40000, 16384])
+    B, k = 2, 16384
+    inp = datagen.make_decode(B, None, FULL, seed=48, lengths=lengths, regime="peaked")
+    d = upload_decode(inp)
+    idx = _random_sets(rng, lengths, k)
+    out = torch.empty((B, FULL.H, FULL.Dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, FULL.H), device="cuda")
+    wsb = dsa.dsa_sparse_mla_decode_workspace_size(B, FULL.H, FULL.Dv, k)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_sparse_mla_decode(dsa.BF16, d.q, dsa.Cache(d.kv, None, d.block_table, d.page_size, d.seq_stride),
+                              tensor(idx), B, FULL.H, FULL.Dqk, FULL.Dv, k, scale, out, lse, ws, wsb)
+    o = out.float().cpu().numpy(); l = lse.cpu().numpy()
+    for b in range(B):
+        o_ref, lse_ref = pipeline.decode_attention(inp, b, idx[b], scale)
+        parity.check_attention(o[b], l[b], o_ref, lse_ref, parity.BF16_ATOL, f"b={b}")
+        assert parity.rel_l2(o[b], o_ref) <= 1e-2
+
+    _case("sparse_mla_decode k = 9000, batch 128 on one shared paged pool")
+    B, k, L, ps = 128, 9000, 12000, 64
+    n_pages = (L + ps - 1) // ps
+    q = rng.standard_normal((B, FULL.H, FULL.Dqk)).astype(np.float32)
+    pool = rng.standard_normal((n_pages * ps, FULL.Dqk)).astype(np.float32)
+    q_bits, pool_bits = datagen.to_bf16_bits(q), datagen.to_bf16_bits(pool)
+    table = np.tile(np.arange(n_pages, dtype=np.int32), (B, 1))
+    idx = np.stack([np.sort(rng.choice(L, size=k, replace=False)).astype(np.int32) for _ in range(B)])
+    out = torch.empty((B, FULL.H, FULL.Dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, FULL.H), device="cuda")
+    wsb = dsa.dsa_sparse_mla_decode_workspace_size(B, FULL.H, FULL.Dv, k)
+    assert wsb == B * 2 * FULL.H * (FULL.Dv * 2 + 8)          # two splits of at most 8192
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    qd = tensor(q_bits)
+    kvd = tensor(pool_bits).view(n_pages, ps, FULL.Dqk)
+    dsa.dsa_sparse_mla_decode(dsa.BF16, qd, dsa.Cache(kvd, None, tensor(table), ps, 0), tensor(idx), B, FULL.H,
+                              FULL.Dqk, FULL.Dv, k, scale, out, lse, ws, wsb)
+    o = out.float().cpu().numpy(); l = lse.cpu().numpy()
+    for b in (0, 77, 127):
+        o_ref, lse_ref = sparse_mla(decode_bf16(q_bits[b]), decode_bf16(pool_bits[idx[b]]), FULL.Dv, scale)
+        parity.check_attention(o[b], l[b], o_ref, lse_ref, parity.BF16_ATOL, f"b={b}")
+        assert parity.rel_l2(o[b], o_ref) <= 1e-2
+
+
+def test_sparse_mla_prefill_largest_k():
+    """Prefill at the bf16 path's limit k = 8192 (a row's whole kept set in one workgroup):
+    rows past t = 8192 keep 8192 of their t + 1 candidates, earlier rows keep all.  64 heads
+    (one head block) keep the inputs small; unscaled N(0,1) data makes attention peaked."""
+    import long_context_sparse_06_amd as dsa
+    from oracle import sparse_mla
+    _case("sparse_mla_prefill k = 8192")
+    rng = np.random.default_rng(49)
+    T, k, H = 8300, 8192, 64
+    q_bits = datagen.to_bf16_bits(rng.standard_normal((T, H, FULL.Dqk)).astype(np.float32))
+    kv_bits = datagen.to_bf16_bits(rng.standard_normal((T, FULL.Dqk)).astype(np.float32))
+    idx = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        m = min(k, t + 1)
+        idx[t, :m] = np.arange(m) if m == t + 1 else np.sort(rng.choice(t + 1, size=m, replace=False))
+    scale = 1.0 / math.sqrt(FULL.Dqk)
+    out = torch.empty((T, H, FULL.Dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), device="cuda")
+    dsa.dsa_sparse_mla_prefill(dsa.BF16, tensor(q_bits), tensor(kv_bits), tensor(idx), T, H, FULL.Dqk, FULL.Dv,
+                               k, scale, out, lse)
+    o = out.float().cpu().numpy(); l = lse.cpu().numpy()
+    for t in (0, 4000, 8191, 8192, 8250, T - 1):
+        sel = idx[t][idx[t] >= 0]
+        o_ref, lse_ref = sparse_mla(decode_bf16(q_bits[t]), decode_bf16(kv_bits[sel]), FULL.Dv, scale)
+        parity.check_attention(o[t], l[t], o_ref, lse_ref, parity.BF16_ATOL, f"t={t}")
+        assert parity.rel_l2(o[t], o_ref) <= 1e-2
 
 
 def test_sparse_mla_empty_and_single():
