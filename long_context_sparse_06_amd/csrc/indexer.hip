@@ -168,7 +168,9 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
 // one contiguous, conflict-free 1 KB; the 64 key scales follow.  Ring of three trips, two in flight; the slots are separate LDS variables and the
 // loop is unrolled by three so every slot is a compile-time variable (the copy wave never
 // reads the ring, the compute waves issue no copies).
-constexpr int kRowsPerWg = 8;
+// Seven rows plus the copy wave make eight waves, so two workgroups fit a CU at this kernel's
+// register use (eight rows and nine waves allowed only one).
+constexpr int kRowsPerWg = 7;
 constexpr int kRowsKernelMin = 512;  // calls with at least this many rows use the kernel below
 constexpr int kRowsThreads = (kRowsPerWg + 1) * WAVE;
 constexpr int kTripBytes = kIdxBatch * 128 + kIdxBatch * 4;
@@ -390,8 +392,8 @@ hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, cons
                                     int64_t ld, hipStream_t s, float* samp, int samp_min_n) {
   const uint8_t* kd = static_cast<const uint8_t*>(keys.data);
   if (R >= kRowsKernelMin && !samp) {
-    // Many rows: eight rows per workgroup sharing staged key trips; 2048 keys per workgroup.
-    const int64_t kpw = 2048;
+    // Many rows: seven rows per workgroup sharing staged key trips; 4096 keys per workgroup.
+    const int64_t kpw = 4096;
     const dim3 grid((unsigned)((R + kRowsPerWg - 1) / kRowsPerWg), (unsigned)((n_bound + kpw - 1) / kpw));
     if (keys.table) {
       const int ps = keys.page_size;

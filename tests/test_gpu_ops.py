@@ -200,15 +200,17 @@ def test_indexer_quality_matches_oracle(paged, regime):
 
 
 # ----------------------------------------------------------------------------- cache append
-@pytest.mark.parametrize("paged", [False, True])
-def test_cache_append_matches_oracle_quantiser(paged):
+@pytest.mark.parametrize("paged,dI,D", [(False, FULL.dI, FULL.Dqk), (True, FULL.dI, FULL.Dqk),
+                                         (False, 4096, 4096), (True, 9, 7)])
+def test_cache_append_matches_oracle_quantiser(paged, dI, D):
     """The new token's key lands as oracle.quantize_key's codes and scale (bit-exact), its
-    latent row as given, and nothing else in either cache changes."""
+    latent row as given, and nothing else in either cache changes; also at the largest row
+    widths accepted (4096) and at odd widths (the latent row copied element by element)."""
     import long_context_sparse_06_amd as dsa
-    _case(f"cache_append paged={paged}")
+    _case(f"cache_append paged={paged} dI={dI} Dqk={D}")
     rng = np.random.default_rng(41)
     lengths = np.array([100, 64, 65, 1, 4000, 257])
-    B, dI, D, ps = len(lengths), FULL.dI, FULL.Dqk, 64
+    B, ps = len(lengths), 64
     k_new = (rng.standard_normal((B, dI)) * 0.3).astype(np.float32)
     k_new[1] = 0.0                                                    # all zero: scale 1
     ties = np.array([448.0, 1.0625, 1.1875, 432.0, 1.5 * 2.0 ** -9, 7.5 * 2.0 ** -9, -1.0625, -0.0],
