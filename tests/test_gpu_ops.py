@@ -138,8 +138,20 @@ def test_index_topk_equals_the_two_calls(paged):
     two rows are also checked against the oracle's top-k under the band rule."""
     import long_context_sparse_06_amd as dsa
     _case(f"index_topk paged={paged}")
-    lengths = np.array([70000, 33000, 40000, 5000, 1500, 2049])
+    lengths = np.array([70000, 33000, 40000, 5000, 1500, 2049, 50000, 45000, 131072])
     inp = datagen.make_decode(len(lengths), None, FULL, seed=51, lengths=lengths, paged=paged)
+
+    def slot(b, s):  # storage index of token s of sequence b in k_scale
+        if inp.block_table is None:
+            return (b, s)
+        ps = inp.page_size
+        return (inp.block_table[b, s // ps], s % ps)
+
+    # Row 6: its top-k sits in one stretch of 2500 tokens (one or two indexer chunks), so that
+    # chunk's local threshold is high and too few candidates reach it: the full-row fallback.
+    for s_ in range(20000, 22500):
+        inp.k_scale[slot(6, s_)] *= np.float32(1000.0)
+    inp.q_idx[7] = 0                                   # row 7: every score 0 (all tied)
     d = upload_decode(inp)
     B, k = d.B, FULL.k
     cache = dsa.Cache(d.keys, d.k_scale, d.block_table, d.page_size, d.seq_stride)
@@ -158,8 +170,9 @@ def test_index_topk_equals_the_two_calls(paged):
     got_np, ref_np = got.cpu().numpy(), ref_idx.cpu().numpy()
     for b in range(B):
         assert np.array_equal(got_np[b], ref_np[b]), f"row {b} (n={lengths[b]}) differs from the two-call path"
-    for b in (0, 3):
+    for b in (0, 3, 6):
         parity.check_index_set(got_np[b], pipeline.decode_scores(inp, b), k, f"row {b}")
+    assert np.array_equal(got_np[7], np.arange(k))     # all tied: lowest indices
 
 
 # ----------------------------------------------------------------------------- indexer quality
