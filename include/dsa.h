@@ -3,8 +3,8 @@
  *
  * The path, as the pages state the problem (MarkTechPost, "DeepSeek V3.2-Exp Cuts
  * Long-Context Costs with DeepSeek Sparse Attention (DSA) While Maintaining
- * Benchmark Parity": two-tier pipeline "FP8 index -> top-k selection -> sparse core
- * attention"; maplevalley.com.cn news 1594152, section "1. 细粒度稀疏架构": a
+ * Benchmark Parity": a two-tier pipeline -- an FP8 indexer, then top-k, then core
+ * attention over the kept tokens; maplevalley.com.cn news 1594152, section "1. 细粒度稀疏架构": a
  * lightning indexer scores every preceding token and each query keeps only k
  * key/value pairs, O(L^2) -> O(Lk)):
  *
@@ -74,7 +74,7 @@ typedef struct {
 
 /*
  * dsa_index_scores -- lightning-indexer scores (first tier of the DSA pipeline:
- * "FP8 index", MarkTechPost article above; "Lightning Indexer", maplevalley article
+ * an FP8 indexer, MarkTechPost article above; the lightning indexer, maplevalley article
  * section 1).  The pages do not print the formula; this library computes
  *
  *   scores[r * ld + s] = k_scale[seq, s] * q_scale[r] * sum_{j < H_I} w[r, j] * max(0, q[r, j, :] . k[seq, s, :])
@@ -118,8 +118,8 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int
 
 /*
  * dsa_sparse_mla_decode -- sparse core attention for one new token per sequence:
- * MLA in MQA mode (MarkTechPost "Instantiation": each latent KV entry is shared across
- * all query heads).  For sequence b and head h, over S_b = { idx[b, j] : idx[b, j] >= 0 }:
+ * MLA in MQA mode (MarkTechPost "Instantiation": one latent KV row serves every query
+ * head).  For sequence b and head h, over S_b = { idx[b, j] : idx[b, j] >= 0 }:
  *
  *   z_s = softmax_scale * q[b, h, :] . kv[b, s, :]          (all Dqk columns)
  *   out[b, h, :] = sum_s softmax(z)_s * kv[b, s, :Dv]        (value = first Dv columns)
@@ -158,8 +158,8 @@ dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, c
                                   void* out, float* lse, hipStream_t stream);
 
 /*
- * dsa_index_topk -- dsa_index_scores followed by dsa_topk in one call (the pages' "FP8 index
- * -> top-k selection" as one stage), with n_valid[r] = row_pos[r] + 1.  The result is exactly
+ * dsa_index_topk -- dsa_index_scores followed by dsa_topk in one call (the pages' first two
+ * steps, indexing then selection, as one stage), with n_valid[r] = row_pos[r] + 1.  The result is exactly
  * that of the two calls (same scores, same selection rule).  Fused: the indexer also stores
  * each long row's 2048 evenly spaced sample scores contiguously, where the top-k's threshold
  * search reads them as one block instead of gathering them from the score row.  Scores,
@@ -181,8 +181,8 @@ dsa_status dsa_index_topk(dsa_dtype dt, const void* q, const float* q_scale, con
 /*
  * dsa_indexer_quality -- forward-only diagnostic of how well the index scores imitate dense
  * attention, the quantity the pages say the indexer is trained on (MarkTechPost article
- * above, "Training signal": the indexer imitates the dense model's head-summed attention
- * distribution through a KL divergence).  For row r with n = row_pos[r] + 1 candidates:
+ * above, "Training signal": a KL loss pulls the indexer towards the dense attention
+ * summed over heads).  For row r with n = row_pos[r] + 1 candidates:
  *   p[s]      = (1/H) sum_h softmax_s(softmax_scale * q[r, h, :] . kv[s, :])   (all s < n)
  *   kl[r]     = sum_s p[s] * (ln p[s] - ln softmax_s(scores[r, s]))   (nats, the dense
  *               distribution as the target)
@@ -205,7 +205,7 @@ dsa_status dsa_indexer_quality(const void* q, const dsa_cache* kv, const float* 
 /*
  * dsa_masked_mla_prefill -- the same result as dsa_sparse_mla_prefill, computed in the
  * dense "masked" form the pages name for short prefill (MarkTechPost article above, "Costs
- * vs. position (128k)": prefill benefits through a masked MHA simulation at short lengths):
+ * vs. position (128k)": short prefills run attention densely under a mask):
  * row t runs over the contiguous positions 0..t in 32-row tiles and masks every position
  * not in its kept set S_t = { idx[t, j] : 0 <= idx[t, j] <= t } (other entries are ignored).
  * No row gather, but the cost grows with t rather than |S_t|: it pays while t + 1 is
@@ -221,7 +221,7 @@ dsa_status dsa_masked_mla_prefill(dsa_dtype dt, const void* q, const void* kv, c
 
 /*
  * dsa_cache_append -- store each row's new token in the two caches before a step reads
- * them: the indexer key (FP8, the pages' "FP8 index", MarkTechPost article above, two-tier
+ * them: the indexer key (FP8, as the pages' indexer runs, MarkTechPost article above, two-tier
  * pipeline) and the latent row (the joint K/V entry MLA attends over, same article,
  * "Instantiation").  For row r the cache slot is (row_seq[r], row_pos[r]); decode writes
  * the new token at n_valid - 1, the position dsa_index_scores and the attention read as

@@ -2,8 +2,8 @@
 // step reads them (decode reads position n - 1 as the query's own token).
 //
 // The pages give the indexer's keys only as "FP8" (MarkTechPost, "DeepSeek V3.2-Exp Cuts
-// Long-Context Costs with DeepSeek Sparse Attention (DSA) ...", the two-tier pipeline
-// "FP8 index -> top-k selection -> sparse core attention"); the storage is this library's
+// Long-Context Costs with DeepSeek Sparse Attention (DSA) ...", the two-tier pipeline whose
+// first tier indexes in FP8); the storage is this library's
 // reading: OCP e4m3 codes with one fp32 scale per token, scale = amax / 448 (1 for an
 // all-zero key), codes = the key divided by the scale, clamped to +-448 and rounded to
 // nearest even.  The latent row (the joint K/V entry of MLA, same article,

@@ -1,7 +1,7 @@
 // Lightning indexer: I[r,s] = k_scale[s] * q_scale[r] * sum_j w[r,j] * ReLU(q[r,j,:] . k[s,:]).
 //
-// The pages give the indexer only as the lightweight FP8 first tier of "FP8 index ->
-// top-k selection -> sparse core attention" (MarkTechPost, "DeepSeek V3.2-Exp Cuts
+// The pages give the indexer only as the lightweight FP8 first tier of the pipeline that
+// then keeps the top-k tokens and attends over them (MarkTechPost, "DeepSeek V3.2-Exp Cuts
 // Long-Context Costs with DeepSeek Sparse Attention (DSA) ...") and as the "Lightning
 // Indexer" that computes lightweight index scores (maplevalley.com.cn news 1594152,
 // section 1); the ReLU-of-per-head-dots form above is this library's reading.

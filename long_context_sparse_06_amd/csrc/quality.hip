@@ -1,7 +1,7 @@
 // Indexer-quality diagnostic: how well the indexer's distribution imitates dense attention.
 //
-// The pages say the indexer is trained to imitate the dense model's head-summed attention
-// distribution through a KL divergence (MarkTechPost, "DeepSeek V3.2-Exp Cuts Long-Context
+// In the pages the indexer learns by matching, under a KL loss, the distribution of the
+// dense attention summed over heads (MarkTechPost, "DeepSeek V3.2-Exp Cuts Long-Context
 // Costs with DeepSeek Sparse Attention (DSA) ...", "Training signal").  For each query row
 // this computes, over its n candidates,
 //   p[s]   = (1/H) sum_h softmax_s(scale * q_h . kv_s)          (dense, head-averaged)

@@ -1,6 +1,7 @@
 """One DSA attention step composed from the three C-ABI calls.
 
-The pages' order -- "FP8 index -> top-k selection -> sparse core attention"
+The pages' order -- an FP8 indexer first, then the top-k choice, then core attention over
+the chosen tokens only
 (MarkTechPost, "DeepSeek V3.2-Exp Cuts Long-Context Costs with DeepSeek Sparse
 Attention (DSA) ...") -- run as dsa_index_scores -> dsa_topk -> dsa_sparse_mla_*.
 These classes only own the intermediate buffers (score rows, kept indices,

@@ -6,7 +6,7 @@ this module.  It shares no code with the HIP path.
 Sources (the pages):
   [MTP] MarkTechPost, "DeepSeek V3.2-Exp Cuts Long-Context Costs with DeepSeek
         Sparse Attention (DSA) While Maintaining Benchmark Parity": the two-tier
-        pipeline "FP8 index -> top-k selection -> sparse core attention"; the
+        pipeline (FP8 indexer, then top-k, then core attention on the kept tokens); the
         "Training signal" paragraph (top-k = 2048); the "Instantiation"
         paragraph (MLA in MQA mode, one latent KV entry shared by all heads).
   [MV]  maplevalley.com.cn news 1594152, section "1. 细粒度稀疏架构" (Lightning
@@ -135,7 +135,7 @@ def attention_pairs(idx_sets) -> int:
 
 
 # ----------------------------------------------------------------------------
-# cache append: the new token's indexer key stored as FP8 ([MTP] "FP8 index")
+# cache append: the new token's indexer key stored as FP8 ([MTP]: the indexer runs in FP8)
 # ----------------------------------------------------------------------------
 E4M3_MAX = 448.0
 
@@ -180,8 +180,8 @@ def quantize_key(x: np.ndarray):
 
 
 # ----------------------------------------------------------------------------
-# indexer-quality diagnostic ([MTP] "Training signal": the indexer imitates the dense
-# model's head-summed attention distribution through a KL divergence)
+# indexer-quality diagnostic ([MTP] "Training signal": a KL loss pulls the indexer's
+# distribution towards the dense attention summed over heads)
 # ----------------------------------------------------------------------------
 def dense_attention_distribution(q: np.ndarray, kv_rows: np.ndarray, scale: float) -> np.ndarray:
     """Head-summed dense attention over n candidate rows, normalised to a distribution.

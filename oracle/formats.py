@@ -7,8 +7,8 @@ Both decoders are written from the format definitions, not from a library cast:
   and S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
   The pages name the indexer's precision only as "FP8" (MarkTechPost, "DeepSeek
   V3.2-Exp Cuts Long-Context Costs with DeepSeek Sparse Attention (DSA) While
-  Maintaining Benchmark Parity", the two-tier pipeline line "FP8 index -> top-k
-  selection -> sparse core attention"); the e4m3fn variant is this build's
+  Maintaining Benchmark Parity", the two-tier pipeline, whose first tier is an FP8
+  indexer); the e4m3fn variant is this library's
   reading (the format gfx950 computes in).
 * bfloat16: the top 16 bits of an IEEE-754 binary32.
 """

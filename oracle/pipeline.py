@@ -2,8 +2,8 @@
 
 Works on the storage bytes the GPU receives (e4m3 codes + fp32 scales, bf16 bit
 patterns) and decodes them with this package's own decoders.  The order of the
-steps is the pages' pipeline "FP8 index -> top-k selection -> sparse core
-attention" (MarkTechPost, "DeepSeek V3.2-Exp Cuts Long-Context Costs with
+steps is the pages' pipeline -- FP8 indexer, then top-k, then core attention over the
+kept tokens (MarkTechPost, "DeepSeek V3.2-Exp Cuts Long-Context Costs with
 DeepSeek Sparse Attention (DSA) ...").
 """
 from __future__ import annotations
