@@ -24,7 +24,7 @@ each call gives the per-stage breakdown (host gaps included).
 the indexer (A2) against the FP8 MFMA peak and the sparse MLA (A6) against the bf16 MFMA peak,
 both as algorithmic flops over each kernel's own event-timed duration.
 
-Prints one JSON line (rank 0, N = 1).  Multi-GPU runs are not part of this build.
+Prints one JSON line (rank 0, N = 1).  The library has no multi-GPU path.
 """
 from __future__ import annotations
 
@@ -66,7 +66,7 @@ def log(*a):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.mode == "prefill":
