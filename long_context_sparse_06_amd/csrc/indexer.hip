@@ -17,6 +17,7 @@ namespace dsa {
 namespace {
 
 constexpr int kIdxWaves = 8;
+typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kIdxBatch = 64;  // keys per wave per loop trip: four 16-key MFMA column groups
 
 // Scores of one trip of 64 keys for 64 heads.  kb[u] holds lane (col, grp)'s 32 key bytes of
@@ -111,9 +112,17 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
 
   // A operand: q[r, 16*ht + col, 32*grp .. 32*grp+31] (e4m3 bytes); result rows held by
   // this lane are heads 16*ht + 4*grp + i.
+  // The row's query (8 KB) and head weights go to LDS once; every wave reads its fragments
+  // there instead of fetching its own copy through L2.
+  __shared__ __attribute__((aligned(16))) uint8_t sq[64 * 128];
+  __shared__ __attribute__((aligned(16))) float sw[64];
+  for (int i = tid; i < 64 * 128 / 16; i += kIdxWaves * WAVE)
+    reinterpret_cast<uint4*>(sq)[i] = reinterpret_cast<const uint4*>(q + (int64_t)r * (64 * 128))[i];
+  if (tid < 64) sw[tid] = w[(int64_t)r * 64 + tid];
+  __syncthreads();
   v8i qa[4];
   float wr[4][4];
-  load_query(q + (int64_t)r * (64 * 128), w + (int64_t)r * 64, col, grp, qa, wr);
+  load_query(sq, sw, col, grp, qa, wr);
   const float qs = q_scale ? q_scale[r] : 1.0f;
   const int per_wave = keys_per_wg / kIdxWaves;
   const int64_t wbeg = wg_begin + (int64_t)wave * per_wave;
@@ -131,13 +140,14 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
 
   for (int64_t s0 = wbeg; s0 < wend; s0 += kIdxBatch) {
     // Addresses are clamped to the last valid key instead of branching, so every load issues.
+    // Keys are read once per call and are streamed with non-temporal loads.
     v8i kb[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t row = row_of(min(s0 + 16 * u + col, wend - 1));
-      const uint4* p = reinterpret_cast<const uint4*>(kdata + row * 128 + 32 * grp);
-      const uint4 a = p[0], b = p[1];
-      kb[u] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+      const v4i* p = reinterpret_cast<const v4i*>(kdata + row * 128 + 32 * grp);
+      const v4i a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+      kb[u] = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
     const int64_t s_out = s0 + lane;  // the key whose score this lane writes
     const float ks = kscale ? kscale[row_of(min(s_out, wend - 1))] : 1.0f;
