@@ -140,13 +140,23 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
 
   for (int64_t s0 = wbeg; s0 < wend; s0 += kIdxBatch) {
     // Addresses are clamped to the last valid key instead of branching, so every load issues.
-    // Keys are read once per call and are streamed with non-temporal loads.
+    // Keys are read once per call.  Contiguous caches stream them with non-temporal loads
+    // (faster here, and the later kernels of the step run faster too); paged caches, whose
+    // keys come in 8 KB pages scattered over the pool, measured slower that way and use
+    // ordinary loads.
     v8i kb[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t row = row_of(min(s0 + 16 * u + col, wend - 1));
       const v4i* p = reinterpret_cast<const v4i*>(kdata + row * 128 + 32 * grp);
-      const v4i a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+      v4i a, b;
+      if (PAGED) {
+        a = p[0];
+        b = p[1];
+      } else {
+        a = __builtin_nontemporal_load(p);
+        b = __builtin_nontemporal_load(p + 1);
+      }
       kb[u] = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
     const int64_t s_out = s0 + lane;  // the key whose score this lane writes
