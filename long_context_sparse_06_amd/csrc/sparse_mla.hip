@@ -144,11 +144,23 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
                                  // then [tiles] bit mask of each tile's live tokens (MASKED:
                                  // the masks only)
   const int HG = H / kHeadsPerWg;
-  int bid = blockIdx.x;
-  const int sp = bid % n_split;
-  bid /= n_split;
-  const int hg = bid % HG;
-  const int r = bid / HG;
+  // The head blocks of one unit (row, token range) read the same latent rows.  The dispatcher
+  // deals consecutive blocks round-robin to the eight XCDs, so blocks b and b + 8 (same XCD)
+  // take two head blocks of one unit while consecutive units still go to consecutive XCDs:
+  // the second workgroup's gathers hit the XCD's L2, and ragged units stay spread evenly.
+  int unit, hg;
+  {
+    const int b = (int)blockIdx.x, full = ((int)gridDim.x / HG) / 8 * 8 * HG;
+    if (b < full) {
+      unit = b / (8 * HG) * 8 + b % 8;
+      hg = (b / 8) % HG;
+    } else {  // the last units when their count is not a multiple of 8
+      unit = full / HG + (b - full) / HG;
+      hg = (b - full) % HG;
+    }
+  }
+  const int sp = unit % n_split;
+  const int r = unit / n_split;
   const int t_begin = MASKED ? 0 : sp * tok_per_split;
   const int t_end = MASKED ? r + 1 : min(k, t_begin + tok_per_split);
   const int n_tok = t_end > t_begin ? t_end - t_begin : 0;
