@@ -286,19 +286,21 @@ def main():
     qws = torch.empty(qw, dtype=torch.uint8, device=dev)
     qkl = torch.empty(B, device=dev)
     qrc = torch.empty(B, device=dev)
+    qkr = torch.empty(B, device=dev)
     qargs = (st0.q, st0.kv, st0.scores, st0.ld, st0.idx, st0.row_seq, st0.row_pos, B, sh.H, sh.Dqk,
              sh.k, scale, qkl, qrc, qws, qw)
-    dsa.dsa_indexer_quality(*qargs)
+    dsa.dsa_indexer_quality(*qargs, kl_rev=qkr)
     q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     q0.record(stream)
     for _ in range(3):
-        dsa.dsa_indexer_quality(*qargs)
+        dsa.dsa_indexer_quality(*qargs, kl_rev=qkr)
     q1.record(stream)
     torch.cuda.synchronize()
     q_us = q0.elapsed_time(q1) * 1e3 / 3
     q_flops = float(L.sum()) * sh.H * sh.Dqk * 2
     quality = {"us": q_us, "logit_flops": q_flops, "TFLOP_s": q_flops / (q_us * 1e6),
-               "kl_mean": float(qkl.mean()), "recall_mean": float(qrc.mean())}
+               "kl_mean": float(qkl.mean()), "kl_rev_mean": float(qkr.mean()),
+               "recall_mean": float(qrc.mean())}
     del qws
 
     # ---- cache append (the step before the indexer): one new token per sequence, written

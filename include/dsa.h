@@ -186,11 +186,13 @@ dsa_status dsa_index_topk(dsa_dtype dt, const void* q, const float* q_scale, con
  *   p[s]      = (1/H) sum_h softmax_s(softmax_scale * q[r, h, :] . kv[s, :])   (all s < n)
  *   kl[r]     = sum_s p[s] * (ln p[s] - ln softmax_s(scores[r, s]))   (nats, the dense
  *               distribution as the target)
+ *   kl_rev[r] = sum_s q[s] * (ln q[s] - ln p[s]), q = softmax_s(scores[r, s])   (the other
+ *               order: the pages do not fix it; +inf where p underflows to 0)
  *   recall[r] = sum of p[s] over the kept set { idx[r, j] : 0 <= idx[r, j] < n }
  *
  *   q [R, H, Dqk] bf16     kv  bf16 latent cache, contiguous or paged (as the decode call)
  *   scores [R, ld] fp32 (as dsa_index_scores wrote them)   idx [R, k] int32 (as dsa_topk)
- *   kl, recall [R] fp32 outputs
+ *   kl, recall [R] fp32 outputs      kl_rev [R] fp32 output or NULL
  *   ws  device workspace of at least dsa_indexer_quality_workspace_size(R, H, ld) bytes (it
  *       holds every head's logits: R * H * ld fp32)
  * Limits: H a multiple of 16 and <= 128, Dqk a multiple of 32 and <= 576 (else
@@ -200,7 +202,8 @@ size_t dsa_indexer_quality_workspace_size(int R, int H, int64_t ld);
 dsa_status dsa_indexer_quality(const void* q, const dsa_cache* kv, const float* scores, int64_t ld,
                                const int32_t* idx, const int32_t* row_seq, const int32_t* row_pos,
                                int R, int H, int Dqk, int k, float softmax_scale, float* kl,
-                               float* recall, void* ws, size_t ws_bytes, hipStream_t stream);
+                               float* recall, float* kl_rev, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
 
 /*
  * dsa_masked_mla_prefill -- the same result as dsa_sparse_mla_prefill, computed in the

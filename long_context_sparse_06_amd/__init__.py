@@ -65,7 +65,7 @@ _SIGS = {
                               _i32, _vp, _vp, _sz, _vp]),
     "dsa_indexer_quality_workspace_size": (_sz, [_i32, _i32, _i64]),
     "dsa_indexer_quality": (_i32, [_vp, ctypes.POINTER(_Cache), _vp, _i64, _vp, _vp, _vp, _i32, _i32,
-                                   _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+                                   _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dsa_masked_mla_prefill": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp]),
     "dsa_cache_append": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, ctypes.POINTER(_Cache),
@@ -219,13 +219,14 @@ def dsa_indexer_quality_workspace_size(R: int, H: int, ld: int) -> int:
 
 def dsa_indexer_quality(q, kv: Cache, scores, ld: int, idx, row_seq, row_pos, R: int, H: int,
                         Dqk: int, k: int, softmax_scale: float, kl, recall, ws, ws_bytes: int = 0,
-                        stream=None):
-    """Per row: KL(dense head-averaged attention || softmax(index scores)) and the kept set's
-    dense attention mass."""
+                        stream=None, kl_rev=None):
+    """Per row: KL(dense head-averaged attention || softmax(index scores)), the kept set's
+    dense attention mass, and (kl_rev, optional) KL in the other order."""
     if ws is not None and not ws_bytes:
         ws_bytes = ws.numel() * ws.element_size()
     c = kv._c()
     _check("dsa_indexer_quality", lib().dsa_indexer_quality(
         _ptr(q), ctypes.byref(c), _ptr(scores), ld, _ptr(idx), _ptr(row_seq), _ptr(row_pos), R, H,
-        Dqk, k, softmax_scale, _ptr(kl), _ptr(recall), _ptr(ws), ws_bytes, _stream(stream)))
+        Dqk, k, softmax_scale, _ptr(kl), _ptr(recall), _ptr(kl_rev), _ptr(ws), ws_bytes,
+        _stream(stream)))
 

@@ -189,7 +189,8 @@ size_t dsa_indexer_quality_workspace_size(int R, int H, int64_t ld) {
 dsa_status dsa_indexer_quality(const void* q, const dsa_cache* kv, const float* scores, int64_t ld,
                                const int32_t* idx, const int32_t* row_seq, const int32_t* row_pos,
                                int R, int H, int Dqk, int k, float softmax_scale, float* kl,
-                               float* recall, void* ws, size_t ws_bytes, hipStream_t stream) {
+                               float* recall, float* kl_rev, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
   if (!q || !kv || !kv->data || !scores || !idx || !row_seq || !row_pos || !kl || !recall)
     return DSA_ERR_NULL;
   if (R <= 0 || H <= 0 || Dqk <= 0 || k <= 0 || ld <= 0 || R > 65535) return DSA_ERR_SHAPE;
@@ -200,7 +201,7 @@ dsa_status dsa_indexer_quality(const void* q, const dsa_cache* kv, const float* 
   if (!ws || ws_bytes < dsa::quality_workspace_bytes(R, H, ld)) return DSA_ERR_WORKSPACE;
   return launched(dsa::launch_indexer_quality(static_cast<const uint16_t*>(q), view(kv), scores, ld, idx, k,
                                               row_seq, row_pos, R, H, Dqk, ld, softmax_scale, kl, recall,
-                                              ws, stream));
+                                              kl_rev, ws, stream));
 }
 
 dsa_status dsa_masked_mla_prefill(dsa_dtype dt, const void* q, const void* kv, const int32_t* idx,

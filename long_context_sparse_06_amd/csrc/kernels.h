@@ -64,6 +64,7 @@ size_t quality_workspace_bytes(int R, int H, int64_t ld);
 hipError_t launch_indexer_quality(const uint16_t* q, const CacheView& kv, const float* scores,
                                   int64_t sld, const int32_t* idx, int k, const int32_t* row_seq,
                                   const int32_t* row_pos, int R, int H, int Dqk, int64_t ld,
-                                  float scale, float* kl, float* recall, void* ws, hipStream_t s);
+                                  float scale, float* kl, float* recall, float* kl_rev, void* ws,
+                                  hipStream_t s);
 
 }  // namespace dsa

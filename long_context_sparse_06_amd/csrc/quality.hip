@@ -6,6 +6,7 @@
 // this computes, over its n candidates,
 //   p[s]   = (1/H) sum_h softmax_s(scale * q_h . kv_s)          (dense, head-averaged)
 //   KL     = sum_s p[s] * (ln p[s] - ln softmax_s(I[s]))          (nats; target first)
+//   KL_rev = sum_s q[s] * (ln q[s] - ln p[s]), q = softmax(I)     (the other order; optional)
 //   recall = sum_{s in kept set} p[s]
 // Forward only: no gradients, nothing here is on the decode path.
 //
@@ -267,19 +268,20 @@ __global__ __launch_bounds__(256) void quality_stats_kernel(const float2* __rest
   }
 }
 
-// Partial sums over one chunk of tokens: KL terms p (ln p - ln q) and the kept set's mass.
+// Partial sums over one chunk of tokens: KL terms p (ln p - ln q) and q (ln q - ln p), and the
+// kept set's mass.
 __global__ __launch_bounds__(256) void quality_partial_kernel(
     const float* __restrict__ z2, const float* __restrict__ scores, int64_t sld,
     const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ row_pos, int H, int64_t ld,
     const float2* __restrict__ stats, const float2* __restrict__ score_stats, int n_sc, int n_chunks,
-    float2* __restrict__ partial) {
+    float4* __restrict__ partial) {
   __shared__ uint32_t kept[kQSumChunk / 32];
   __shared__ float2 hst[129];  // per head: (max, 1 / sum); then the index scores' (max, sum)
-  __shared__ float red_kl[256], red_rc[256];
+  __shared__ float red_kl[256], red_rc[256], red_kr[256];
   const int r = blockIdx.x / n_chunks;
   const int64_t c0 = (int64_t)(blockIdx.x % n_chunks) * kQSumChunk;
   const int64_t n = (int64_t)row_pos[r] + 1;
-  float kl = 0.0f, rc = 0.0f;
+  float kl = 0.0f, rc = 0.0f, kr = 0.0f;
   if (c0 < n) {
     for (int i = threadIdx.x; i < kQSumChunk / 32; i += 256) kept[i] = 0u;
     for (int h = threadIdx.x; h < H; h += 256) {
@@ -316,47 +318,61 @@ __global__ __launch_bounds__(256) void quality_partial_kernel(
       }
       p *= 1.0f / (float)H;
       const float log_q = (scores[(int64_t)r * sld + s] * kLog2e - si.x) * kLn2f - ln_li;
-      if (p > 0.0f) kl += p * (logf(p) - log_q);
+      const float q = expf(log_q);
+      if (p > 0.0f) {
+        const float ln_p = logf(p);
+        kl += p * (ln_p - log_q);
+        kr += q * (log_q - ln_p);
+      } else if (q > 0.0f) {
+        kr = INFINITY;  // the dense target has a zero the indexer does not
+      }
       if ((kept[(s - c0) >> 5] >> ((s - c0) & 31)) & 1u) rc += p;
     }
   }
   red_kl[threadIdx.x] = kl;
   red_rc[threadIdx.x] = rc;
+  red_kr[threadIdx.x] = kr;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
     if ((int)threadIdx.x < o) {
       red_kl[threadIdx.x] += red_kl[threadIdx.x + o];
       red_rc[threadIdx.x] += red_rc[threadIdx.x + o];
+      red_kr[threadIdx.x] += red_kr[threadIdx.x + o];
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) partial[blockIdx.x] = make_float2(red_kl[0], red_rc[0]);
+  if (threadIdx.x == 0) partial[blockIdx.x] = make_float4(red_kl[0], red_rc[0], red_kr[0], 0.0f);
 }
 
-__global__ __launch_bounds__(256) void quality_finish_kernel(const float2* __restrict__ partial,
+__global__ __launch_bounds__(256) void quality_finish_kernel(const float4* __restrict__ partial,
                                                              int n_chunks, float* __restrict__ kl,
-                                                             float* __restrict__ recall) {
-  __shared__ float a[256], b[256];
+                                                             float* __restrict__ recall,
+                                                             float* __restrict__ kl_rev) {
+  __shared__ float a[256], b[256], c3[256];
   const int r = blockIdx.x;
-  float x = 0.0f, y = 0.0f;
+  float x = 0.0f, y = 0.0f, z = 0.0f;
   for (int c = threadIdx.x; c < n_chunks; c += 256) {
-    const float2 v = partial[(int64_t)r * n_chunks + c];
+    const float4 v = partial[(int64_t)r * n_chunks + c];
     x += v.x;
     y += v.y;
+    z += v.z;
   }
   a[threadIdx.x] = x;
   b[threadIdx.x] = y;
+  c3[threadIdx.x] = z;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
     if ((int)threadIdx.x < o) {
       a[threadIdx.x] += a[threadIdx.x + o];
       b[threadIdx.x] += b[threadIdx.x + o];
+      c3[threadIdx.x] += c3[threadIdx.x + o];
     }
     __syncthreads();
   }
   if (threadIdx.x == 0) {
     kl[r] = a[0];
     recall[r] = b[0];
+    if (kl_rev) kl_rev[r] = c3[0];
   }
 }
 
@@ -371,7 +387,7 @@ QualityWs quality_ws(int R, int H, int64_t ld) {
   L.stats = L.span_stats + up(sizeof(float2) * (size_t)R * H * (size_t)((ld + kQSpan - 1) / kQSpan));
   L.score_stats = L.stats + up(sizeof(float2) * (size_t)R * H);
   L.partial = L.score_stats + up(sizeof(float2) * (size_t)R * (size_t)((ld + kQScoreChunk - 1) / kQScoreChunk));
-  L.total = L.partial + up(sizeof(float2) * (size_t)R * (size_t)((ld + kQSumChunk - 1) / kQSumChunk));
+  L.total = L.partial + up(sizeof(float4) * (size_t)R * (size_t)((ld + kQSumChunk - 1) / kQSumChunk));
   return L;
 }
 
@@ -382,14 +398,15 @@ size_t quality_workspace_bytes(int R, int H, int64_t ld) { return quality_ws(R, 
 hipError_t launch_indexer_quality(const uint16_t* q, const CacheView& kv, const float* scores,
                                   int64_t sld, const int32_t* idx, int k, const int32_t* row_seq,
                                   const int32_t* row_pos, int R, int H, int Dqk, int64_t ld,
-                                  float scale, float* kl, float* recall, void* ws, hipStream_t s) {
+                                  float scale, float* kl, float* recall, float* kl_rev, void* ws,
+                                  hipStream_t s) {
   const QualityWs L = quality_ws(R, H, ld);
   char* b = static_cast<char*>(ws);
   float* z2 = reinterpret_cast<float*>(b + L.z2);
   float2* span_stats = reinterpret_cast<float2*>(b + L.span_stats);
   float2* stats = reinterpret_cast<float2*>(b + L.stats);
   float2* score_stats = reinterpret_cast<float2*>(b + L.score_stats);
-  float2* partial = reinterpret_cast<float2*>(b + L.partial);
+  float4* partial = reinterpret_cast<float4*>(b + L.partial);
   const int nsp = (int)((ld + kQSpan - 1) / kQSpan);
   quality_logits_kernel<<<(unsigned)R * (unsigned)nsp, kQThreads, 0, s>>>(
       q, static_cast<const uint16_t*>(kv.data), kv.table, kv.page_size, kv.max_pages, kv.seq_stride,
@@ -404,7 +421,7 @@ hipError_t launch_indexer_quality(const uint16_t* q, const CacheView& kv, const 
   quality_partial_kernel<<<(unsigned)R * (unsigned)ns, 256, 0, s>>>(z2, scores, sld, idx, k, row_pos, H, ld,
                                                                    stats, score_stats, nsc, ns, partial);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  quality_finish_kernel<<<R, 256, 0, s>>>(partial, ns, kl, recall);
+  quality_finish_kernel<<<R, 256, 0, s>>>(partial, ns, kl, recall, kl_rev);
   return hipGetLastError();
 }
 

@@ -13,13 +13,13 @@ the pages -- the indexer's formula itself (ReLU of per-head dots, weighted by w
 and scaled per token): parity is against this reading only.
 """
 from .dsa import (attention_pairs, dense_attention_distribution, dense_causal_mla, encode_e4m3,
-                  index_scores, indexer_quality, kth_score, logical_rows, quantize_key,
-                  sparse_mla, topk)
+                  index_scores, indexer_kl_reverse, indexer_quality, kth_score, logical_rows,
+                  quantize_key, sparse_mla, topk)
 from .formats import E4M3_TABLE, decode_bf16, decode_e4m3
 from . import pipeline
 
 __all__ = [
     "attention_pairs", "dense_attention_distribution", "dense_causal_mla", "encode_e4m3",
-    "index_scores", "indexer_quality", "kth_score",
+    "index_scores", "indexer_kl_reverse", "indexer_quality", "kth_score",
     "logical_rows", "quantize_key", "sparse_mla", "topk", "E4M3_TABLE", "decode_bf16", "decode_e4m3", "pipeline",
 ]

@@ -213,3 +213,15 @@ def indexer_quality(p_attn: np.ndarray, scores: np.ndarray, kept) -> tuple:
     recall = float(p[kept].sum())
     return kl, recall
 
+
+def indexer_kl_reverse(p_attn: np.ndarray, scores: np.ndarray) -> float:
+    """KL(softmax(scores) || p_attn) in nats: the other direction of the diagnostic's KL (the
+    pages name a KL term without fixing its order).  Infinite where p_attn = 0 < softmax."""
+    p = np.asarray(p_attn, dtype=np.float64)
+    i = np.asarray(scores, dtype=np.float64)
+    log_q = i - i.max()
+    log_q = log_q - np.log(np.exp(log_q).sum())
+    q = np.exp(log_q)
+    with np.errstate(divide="ignore"):
+        return float(np.sum(q * (log_q - np.log(p))))
+

@@ -10,8 +10,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .dsa import (dense_attention_distribution, index_scores, indexer_quality, logical_rows,
-                  sparse_mla, topk)
+from .dsa import (dense_attention_distribution, index_scores, indexer_kl_reverse, indexer_quality,
+                  logical_rows, sparse_mla, topk)
 from .formats import decode_bf16, decode_e4m3
 
 
@@ -110,12 +110,14 @@ def prefill(inp, scale: float, k: int = None, rows=None):
     return out
 
 
-def decode_indexer_quality(inp, b: int, scale: float, kept, scores=None):
+def decode_indexer_quality(inp, b: int, scale: float, kept, scores=None, reverse=False):
     """KL(dense head-summed attention || softmax(index scores)) and the kept set's attention
-    mass for sequence b's query (all L_b cached tokens are candidates)."""
+    mass for sequence b's query (all L_b cached tokens are candidates); with `reverse`, also
+    KL(softmax(index scores) || dense), returned third."""
     L = int(inp.lengths[b])
     rows = decode_kv_rows(inp, b, np.arange(L))
     p = dense_attention_distribution(_dec_lat(inp.q[b]), rows, scale)
     s = decode_scores(inp, b) if scores is None else np.asarray(scores, dtype=np.float64)
-    return indexer_quality(p, s, kept)
+    kl, recall = indexer_quality(p, s, kept)
+    return (kl, recall, indexer_kl_reverse(p, s)) if reverse else (kl, recall)
 

@@ -96,10 +96,10 @@ def test_host_validation_paths():
     # indexer-quality diagnostic
     qw = L.dsa_indexer_quality_workspace_size(8, 128, 4096)
     assert qw >= 8 * 128 * 4096 * 4
-    assert L.dsa_indexer_quality(None, ctypes.byref(kv), FAKE, 4096, FAKE, FAKE, FAKE, 8, 128, 576, 2048, 0.04, FAKE, FAKE, FAKE, qw, None) == 1
-    assert L.dsa_indexer_quality(FAKE, ctypes.byref(kv), FAKE, 4096, FAKE, FAKE, FAKE, 8, 120, 576, 2048, 0.04, FAKE, FAKE, FAKE, qw, None) == 6
-    assert L.dsa_indexer_quality(FAKE, ctypes.byref(kv), FAKE, 1024, FAKE, FAKE, FAKE, 8, 128, 576, 2048, 0.04, FAKE, FAKE, FAKE, qw, None) == 2
-    assert L.dsa_indexer_quality(FAKE, ctypes.byref(kv), FAKE, 4096, FAKE, FAKE, FAKE, 8, 128, 576, 2048, 0.04, FAKE, FAKE, FAKE, qw - 1, None) == 4
+    assert L.dsa_indexer_quality(None, ctypes.byref(kv), FAKE, 4096, FAKE, FAKE, FAKE, 8, 128, 576, 2048, 0.04, FAKE, FAKE, None, FAKE, qw, None) == 1
+    assert L.dsa_indexer_quality(FAKE, ctypes.byref(kv), FAKE, 4096, FAKE, FAKE, FAKE, 8, 120, 576, 2048, 0.04, FAKE, FAKE, None, FAKE, qw, None) == 6
+    assert L.dsa_indexer_quality(FAKE, ctypes.byref(kv), FAKE, 1024, FAKE, FAKE, FAKE, 8, 128, 576, 2048, 0.04, FAKE, FAKE, None, FAKE, qw, None) == 2
+    assert L.dsa_indexer_quality(FAKE, ctypes.byref(kv), FAKE, 4096, FAKE, FAKE, FAKE, 8, 128, 576, 2048, 0.04, FAKE, FAKE, None, FAKE, qw - 1, None) == 4
     # cache append
     ks = dsa._Cache(FAKE, FAKE, None, 0, 0, 1024)
     noscale = dsa._Cache(FAKE, None, None, 0, 0, 1024)

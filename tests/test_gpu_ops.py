@@ -179,7 +179,8 @@ def test_index_topk_equals_the_two_calls(paged):
 @pytest.mark.parametrize("paged,regime", [(False, "peaked"), (True, "gaussian")])
 def test_indexer_quality_matches_oracle(paged, regime):
     """KL(dense head-averaged attention || softmax(scores)) and the kept set's attention mass
-    per row, against the oracle fed the same scores and kept sets the GPU produced."""
+    per row, against the oracle fed the same scores and kept sets the GPU produced; KL in the
+    other order too (its output is optional: requested in one case, NULL in the other)."""
     import long_context_sparse_06_amd as dsa
     _case(f"indexer_quality paged={paged} {regime}")
     lengths = np.array([5000, 2049, 300, 12000])
@@ -199,16 +200,23 @@ def test_indexer_quality_matches_oracle(paged, regime):
     ws = torch.empty(qw, dtype=torch.uint8, device="cuda")
     kl = torch.full((B,), float("nan"), device="cuda")
     rc = torch.full((B,), float("nan"), device="cuda")
+    want_rev = not paged
+    klr = torch.full((B,), float("nan"), device="cuda") if want_rev else None
     dsa.dsa_indexer_quality(d.q, cache_v, scores, d.ld, idx, d.row_seq, d.row_pos, B, FULL.H, FULL.Dqk,
-                            k, scale, kl, rc, ws, qw)
+                            k, scale, kl, rc, ws, qw, kl_rev=klr)
     kl_g, rc_g = kl.cpu().numpy(), rc.cpu().numpy()
     s_np, i_np = scores.cpu().numpy(), idx.cpu().numpy()
     for b in range(B):
         L = int(lengths[b])
-        kl_r, rc_r = pipeline.decode_indexer_quality(inp, b, scale, i_np[b], scores=s_np[b, :L])
+        kl_r, rc_r, kr_r = pipeline.decode_indexer_quality(inp, b, scale, i_np[b], scores=s_np[b, :L],
+                                                           reverse=True)
         print(f"  row {b}: kl {kl_g[b]:.6f} / {kl_r:.6f}  recall {rc_g[b]:.6f} / {rc_r:.6f}", flush=True)
         assert abs(kl_g[b] - kl_r) <= 1e-4 * abs(kl_r) + 2e-5, f"row {b}: kl {kl_g[b]} vs {kl_r}"
         assert abs(rc_g[b] - rc_r) <= 1e-4 * rc_r + 1e-6, f"row {b}: recall {rc_g[b]} vs {rc_r}"
+        if want_rev:
+            kr_g = float(klr[b])
+            print(f"         kl_rev {kr_g:.6f} / {kr_r:.6f}", flush=True)
+            assert abs(kr_g - kr_r) <= 1e-4 * abs(kr_r) + 2e-5, f"row {b}: kl_rev {kr_g} vs {kr_r}"
     assert abs(rc_g[2] - 1.0) < 1e-5          # n = 300 <= k: every candidate is kept
 
 

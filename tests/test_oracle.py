@@ -378,3 +378,22 @@ def test_indexer_quality_closed_forms_and_scipy_entropy():
     kl2, rec2 = oracle.indexer_quality(p2, np.zeros(2), [1])
     assert abs(kl2 - (0.25 * np.log(0.5) + 0.75 * np.log(1.5))) < 1e-15 and abs(rec2 - 0.75) < 1e-15
 
+
+
+def test_indexer_kl_reverse_pins():
+    """The other KL direction, KL(softmax(scores) || p): scipy's relative entropy with the
+    arguments swapped, zero for scores = log p + c, a two-token case by hand, and infinity
+    where the target has a zero the indexer does not."""
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    rng = np.random.default_rng(63)
+    p = softmax(rng.standard_normal(40))
+    s = rng.standard_normal(40) * 3
+    klr = oracle.indexer_kl_reverse(p, s)
+    assert abs(klr - entropy(softmax(s), p)) < 1e-12 and klr >= 0
+    assert abs(klr - oracle.indexer_quality(p, s, [])[0]) > 1e-3       # not the forward KL
+    assert abs(oracle.indexer_kl_reverse(p, np.log(p) - 2.5)) < 1e-12
+    # q = softmax(0, ln 3) = (1/4, 3/4) against p = (1/2, 1/2): (1/4) ln(1/2) + (3/4) ln(3/2)
+    klr2 = oracle.indexer_kl_reverse(np.array([0.5, 0.5]), np.array([0.0, np.log(3.0)]))
+    assert abs(klr2 - (0.25 * np.log(0.5) + 0.75 * np.log(1.5))) < 1e-15
+    assert np.isinf(oracle.indexer_kl_reverse(np.array([1.0, 0.0]), np.zeros(2)))
