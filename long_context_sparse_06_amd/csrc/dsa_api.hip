@@ -170,10 +170,13 @@ dsa_status dsa_index_topk(dsa_dtype dt, const void* q, const float* q_scale, con
   const dsa::CacheView kv = view(keys);
   hipError_t e;
   if (dt == DSA_E4M3 && H_I == 64 && d_I == 128) {
+    // Decode-sized calls get the indexer's contiguous sample; calls with many rows (prefill)
+    // keep the many-rows indexer, and the top-k draws its sample from the score rows.
+    float* sp = R < dsa::index_rows_kernel_min() ? samp : nullptr;
     e = dsa::launch_index_fp8_h64d128(static_cast<const uint8_t*>(q), q_scale, w, kv, row_seq, row_pos,
-                                      R, cap, scores, cap, stream, samp, dsa::topk_long_row_min());
+                                      R, cap, scores, cap, stream, sp, dsa::topk_long_row_min());
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
-    return launched(dsa::launch_topk(scores, cap, row_pos, R, k, idx, tws, stream, samp, 1));
+    return launched(dsa::launch_topk(scores, cap, row_pos, R, k, idx, tws, stream, sp, 1));
   }
   e = dsa::launch_index_generic(dt == DSA_E4M3, q, q_scale, w, kv, row_seq, row_pos, R, H_I, d_I, cap,
                                 scores, cap, stream);

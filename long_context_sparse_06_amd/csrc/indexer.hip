@@ -406,6 +406,8 @@ __global__ __launch_bounds__(256) void index_generic_kernel(
 
 }  // namespace
 
+int index_rows_kernel_min() { return kRowsKernelMin; }
+
 hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, const float* w,
                                     const CacheView& keys, const int32_t* row_seq,
                                     const int32_t* row_pos, int R, int64_t n_bound, float* scores,

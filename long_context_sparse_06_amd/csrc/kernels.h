@@ -19,6 +19,8 @@ struct CacheView {
 // samp (optional): rows longer than samp_min_n also store their 2048 evenly spaced sample
 // scores contiguously in samp[R, 2048] (positions (i * n) / 2048); the rows kernel for many
 // rows is not used then.
+// Calls with at least this many rows (and no sample wanted) use the many-rows kernel.
+int index_rows_kernel_min();
 hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, const float* w,
                                     const CacheView& keys, const int32_t* row_seq,
                                     const int32_t* row_pos, int R, int64_t n_bound, float* scores,

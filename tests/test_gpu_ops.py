@@ -175,6 +175,44 @@ def test_index_topk_equals_the_two_calls(paged):
     assert np.array_equal(got_np[7], np.arange(k))     # all tied: lowest indices
 
 
+def test_index_topk_many_rows():
+    """A fused call with prefill-many rows (600 queries of one 40000-token sequence at spread
+    positions, so long, mid and short rows) takes the many-rows indexer and the top-k's own
+    sampling; it must equal the two separate calls, and one long row is checked against the
+    oracle's top-k under the band rule."""
+    import long_context_sparse_06_amd as dsa
+    from oracle import index_scores
+    _case("index_topk 600 rows of one sequence")
+    rng = np.random.default_rng(52)
+    L, R, k = 40000, 600, FULL.k
+    inp = datagen.make_decode(1, None, FULL, seed=53, lengths=np.array([L]))
+    d = upload_decode(inp)
+    q_codes = (rng.integers(0, 256, (R, FULL.HI, FULL.dI)) & 0x77).astype(np.uint8)   # finite e4m3
+    q_scale = rng.uniform(0.5, 1.5, R).astype(np.float32)
+    w = rng.uniform(0.0, 1.0, (R, FULL.HI)).astype(np.float32)
+    pos = np.sort(rng.choice(L, R, replace=False)).astype(np.int32)
+    pos[-1] = L - 1
+    qd, qsd, wd = tensor(q_codes), tensor(q_scale), tensor(w)
+    seq_d, pos_d = tensor(np.zeros(R, np.int32)), tensor(pos)
+    cache = dsa.Cache(d.keys, d.k_scale, None, 0, d.seq_stride)
+    scores = torch.empty((R, L), device="cuda")
+    dsa.dsa_index_scores(dsa.E4M3, qd, qsd, wd, cache, seq_d, pos_d, R, FULL.HI, FULL.dI, scores, L)
+    ref_idx = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    tw = dsa.dsa_topk_workspace_size(R, L, k)
+    dsa.dsa_topk(scores, L, tensor(pos + 1), R, k, ref_idx, torch.empty(max(tw, 1), dtype=torch.uint8,
+                                                                          device="cuda"), tw)
+    fw = dsa.dsa_index_topk_workspace_size(R, L, k)
+    fws = torch.empty(fw, dtype=torch.uint8, device="cuda")
+    got = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    dsa.dsa_index_topk(dsa.E4M3, qd, qsd, wd, cache, seq_d, pos_d, R, FULL.HI, FULL.dI, k, got, fws, fw)
+    got_np = got.cpu().numpy()
+    assert np.array_equal(got_np, ref_idx.cpu().numpy()), "fused call differs from the two calls"
+    keys, ks = pipeline.decode_keys(inp, 0)
+    r = R - 1
+    ref = index_scores(decode_e4m3(q_codes[r]), float(q_scale[r]), w[r], keys, ks)
+    parity.check_index_set(got_np[r], ref, k, f"row {r}")
+
+
 # ----------------------------------------------------------------------------- indexer quality
 @pytest.mark.parametrize("paged,regime", [(False, "peaked"), (True, "gaussian")])
 def test_indexer_quality_matches_oracle(paged, regime):
