@@ -519,17 +519,26 @@ __device__ __forceinline__ void select_survivors(const uint32_t* keys, const int
   } else if (bcnt <= kTieMax) {
     // Rank the keys of bin b* by (key descending, position ascending); the one of rank
     // need-1 is the threshold T, and need - (keys of the bin above T) of those equal to T
-    // are taken, lowest position first -- the same rule the emit pass applies.
+    // are taken, lowest position first -- the same rule as emit_selected.  The pass that
+    // gathers the bin's keys already walks the survivors in the emit pass's wave ranges and
+    // counts each range's keys above the bin, and the bin's own keys are all in `ties`, so
+    // the emit needs no counting pass and no barrier of its own.
     const uint64_t bin_end = (uint64_t)t_lo + ((uint64_t)1 << shift) - 1;  // may pass 2^32
     const uint32_t t_hi = (bstar == kSurvBins - 1 || bin_end > 0xFFFFFFFFull) ? 0xFFFFFFFFu : (uint32_t)bin_end;
-    for (int i0 = 0; i0 < total; i0 += kResolveThreads * 4) {
+    const int per = ((total + NW - 1) / NW + WAVE - 1) / WAVE * WAVE;
+    const int beg = w * per;
+    const int end = min(total, beg + per);
+    int above_w = 0;
+    for (int i0 = beg; i0 < end; i0 += 4 * WAVE) {
       uint32_t kv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) kv[u] = keys[min(i0 + u * kResolveThreads + tid, total - 1)];
+      for (int u = 0; u < 4; ++u) kv[u] = keys[min(i0 + u * WAVE + lane, end - 1)];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kResolveThreads + tid;
-        const bool in = (i < total) & (kv[u] >= t_lo) & (kv[u] <= t_hi);
+        const int i = i0 + u * WAVE + lane;
+        const bool ok = i < end;
+        above_w += __popcll(ballot(ok & (kv[u] > t_hi)));
+        const bool in = ok & (kv[u] >= t_lo) & (kv[u] <= t_hi);
         const uint64_t im = ballot(in);
         if (im) {  // one slot reservation per wave and round
           int slot = 0;
@@ -539,6 +548,7 @@ __device__ __forceinline__ void select_survivors(const uint32_t* keys, const int
         }
       }
     }
+    if (lane == 0) st.wtot[0][w] = above_w;
     __syncthreads();
     if (tid < bcnt) {
       const uint2 me = ties[tid];
@@ -554,7 +564,44 @@ __device__ __forceinline__ void select_survivors(const uint32_t* keys, const int
       }
     }
     __syncthreads();
-    th = Threshold{st.tie_T, st.tie_need, false, 0u};
+    const uint32_t T = st.tie_T;
+    const int tneed = st.tie_need;
+    // Selected before this wave's range: every range's keys above the bin, the bin's keys
+    // above T at lower positions, and the first of those equal to T (up to tneed).
+    int g = 0, b = 0;
+    for (int e0 = 0; e0 < bcnt; e0 += WAVE) {
+      const int e = e0 + lane;
+      const uint2 o = ties[min(e, bcnt - 1)];
+      const bool ok = (e < bcnt) & ((int)o.y < beg);
+      g += __popcll(ballot(ok & (o.x > T)));
+      b += __popcll(ballot(ok & (o.x == T)));
+    }
+    const int ab_v = lane < NW ? st.wtot[0][lane] : 0;
+    const int ab_before = readlane(wave_incl_scan(ab_v) - ab_v, w);
+    int sel_run = ab_before + g + min(b, tneed);
+    int eq_run = b;
+    for (int i0 = beg; i0 < end; i0 += 4 * WAVE) {
+      uint32_t kv[4];
+      int iv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = min(i0 + u * WAVE + lane, end - 1);
+        kv[u] = keys[e];
+        iv[u] = ids[e];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = i0 + u * WAVE + lane < end;
+        const bool eq = ok & (kv[u] == T);
+        const uint64_t eqm = ballot(eq);
+        const bool sel = (ok & (kv[u] > T)) | (eq & (eq_run + mask_rank(eqm) < tneed));
+        const uint64_t selm = ballot(sel);
+        if (sel) out[sel_run + mask_rank(selm)] = iv[u];
+        eq_run += __popcll(eqm);
+        sel_run += __popcll(selm);
+      }
+    }
+    return;
   } else {
     __syncthreads();  // every wave has read the survivor histogram before the radix select clears it
     th = find_threshold<kResolveThreads>(src, total, k, hist, st);
@@ -666,11 +713,27 @@ __device__ void resolve_long_row(const float* __restrict__ row, int ld, int n, i
   const uint32_t* rc = counts + (int64_t)r * max_chunks;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const RowHeader rh = hdr[r];
+  // The first 64 chunk counts (wave 0), then -- before any count is known -- the first
+  // U * WAVE candidate slots of this wave's first kPre chunks (slots past a chunk's count
+  // hold stale pairs and are dropped below).  The count load goes first, so waiting for it
+  // leaves the candidate loads in flight, and a typical row's gather costs the one round
+  // trip these loads share.
+  constexpr int U = 4, kPre = 2;
+  const uint2* rcand = cand + (int64_t)r * ld;
+  const int c0 = (w == 0 && lane < nch) ? (int)rc[lane] : 0;
+  uint2 pre[kPre][U];
+#pragma unroll
+  for (int m = 0; m < kPre; ++m) {
+    const int j = w + m * NW < nch ? w + m * NW : 0;
+    const int cl = min(kChunk, n - j * kChunk);  // the chunk's length: slots stay in the row
+#pragma unroll
+    for (int u = 0; u < U; ++u) pre[m][u] = rcand[(int64_t)j * kChunk + min(u * WAVE + lane, cl - 1)];
+  }
   if (w == 0) {  // exclusive prefix of the survivor counts, 64 chunks per step
     int carry = 0;
     for (int j0 = 0; j0 < nch; j0 += WAVE) {
       const int j = j0 + lane;
-      const int cj = j < nch ? (int)rc[j] : 0;
+      const int cj = j0 == 0 ? c0 : (j < nch ? (int)rc[j] : 0);
       const int incl = wave_incl_scan(cj);
       if (j < nch) offs[j] = carry + incl - cj;
       carry += __shfl(incl, WAVE - 1);
@@ -688,13 +751,27 @@ __device__ void resolve_long_row(const float* __restrict__ row, int ld, int n, i
     return;
   }
   {
-    // Wave w copies chunks w, w + NW, ...; each lane issues up to U loads per chunk group
-    // before storing, so typical chunks (~2k/32 survivors) cost one round trip.
-    const uint2* rcand = cand + (int64_t)r * ld;
-    constexpr int U = 4;
+    // Wave w copies chunks w, w + NW, ...: the preloaded slots first, then (for chunks
+    // with more survivors, or beyond the first kPre) U loads per lane per round trip.
+#pragma unroll
+    for (int m = 0; m < kPre; ++m) {
+      const int j = w + m * NW;
+      if (j < nch) {
+        const int o = offs[j], cj = min(offs[j + 1] - o, U * WAVE);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = u * WAVE + lane;
+          if (i < cj) {
+            keys[o + i] = pre[m][u].x;
+            ids[o + i] = (int)pre[m][u].y;
+            atomicAdd(&hist[min((pre[m][u].x - rh.theta) >> rh.shift, (uint32_t)(kSurvBins - 1))], 1);
+          }
+        }
+      }
+    }
     for (int j = w; j < nch; j += NW) {
       const int o = offs[j], cj = offs[j + 1] - o;
-      for (int i0 = 0; i0 < cj; i0 += U * WAVE) {
+      for (int i0 = j < w + kPre * NW ? U * WAVE : 0; i0 < cj; i0 += U * WAVE) {
         uint2 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) v[u] = rcand[(int64_t)j * kChunk + min(i0 + u * WAVE + lane, cj - 1)];
