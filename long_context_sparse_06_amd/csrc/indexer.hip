@@ -28,15 +28,21 @@ __device__ __forceinline__ float trip_scores(const v8i (&qa)[4], const float (&w
   float part[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    float sum = 0.0f;
+    // The four head groups' products go out back to back into separate accumulators, so the
+    // ReLU-weight epilogue of one overlaps the MFMAs still in flight instead of waiting on each.
+    v4f acc[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
-      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
       // cbsz/blgp = 0: both operands OCP e4m3; scale exponent 127 = x1.
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb[u], acc, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sum = fmaf(wr[ht][i], __builtin_amdgcn_fmed3f(acc[i], 0.0f, 3.0e38f), sum);
+      acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb[u], v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                 0, 0, 0, 127, 0, 127);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the four MFMAs ahead of the epilogue
+    float sum = 0.0f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum = fmaf(wr[ht][i], __builtin_amdgcn_fmed3f(acc[ht][i], 0.0f, 3.0e38f), sum);
     part[u] = sum;
   }
   // Stage 1 (lanes l, l^32): lower half keeps groups 0/1, upper half 2/3.
