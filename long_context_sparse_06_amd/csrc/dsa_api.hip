@@ -174,7 +174,7 @@ dsa_status dsa_index_topk(dsa_dtype dt, const void* q, const float* q_scale, con
     // keep the many-rows indexer, and the top-k draws its sample from the score rows.
     float* sp = R < dsa::index_rows_kernel_min() ? samp : nullptr;
     e = dsa::launch_index_fp8_h64d128(static_cast<const uint8_t*>(q), q_scale, w, kv, row_seq, row_pos,
-                                      R, cap, scores, cap, stream, sp, dsa::topk_long_row_min());
+                                      R, cap, scores, cap, stream, sp, dsa::topk_long_row_min(cap));
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     return launched(dsa::launch_topk(scores, cap, row_pos, R, k, idx, tws, stream, sp, 1));
   }

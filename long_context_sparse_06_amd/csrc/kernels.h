@@ -40,8 +40,9 @@ bool topk_shape_ok(int R, int64_t ld);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
                        int32_t* idx, void* ws, hipStream_t s, const float* samp = nullptr,
                        int n_off = 0);
-// Rows longer than this use the sampled compaction (and so want the indexer's sample).
-int topk_long_row_min();
+// Rows longer than this use the sampled compaction (and so want the indexer's sample), for
+// score rows of leading dimension ld.
+int topk_long_row_min(int64_t ld);
 
 // ---- sparse MLA
 size_t mla_decode_workspace_bytes(int B, int H, int Dv, int k);

@@ -15,8 +15,9 @@
 // ballots, so the elements equal to T are taken lowest index first and the output comes
 // out sorted.
 //
-// Rows up to kRowMax scores are selected by one workgroup that holds the row in registers
-// (read from memory once) and keeps only the histograms in LDS.  Longer rows
+// Rows up to kRowMax scores (up to kLongMinWs when the call's rows are longer than kRowMax, so
+// the compaction workspace exists) are selected by one workgroup that holds the row in
+// registers (read from memory once) and keeps only the histograms in LDS.  Longer rows
 // (decode at 128k context) take three launches: one workgroup per row draws an evenly
 // spaced sample and sets a threshold theta whose expected survivor count is ~2k; many
 // workgroups per row compact the survivors (in index order); one workgroup per row then
@@ -36,6 +37,10 @@ namespace {
 constexpr int kRowMax = 32768;     // longest row selected by one workgroup (32 keys per thread)
 constexpr int kSample = 2048;      // sample size for longer rows
 constexpr int kChunk = 4096;       // scores per workgroup in the long-row compaction pass
+// When the call has a candidate workspace (ld > kRowMax), rows longer than this already take
+// the sampled compaction: a single workgroup's multi-pass radix select over 8k..32k scores
+// is slower than the compaction and resolve.
+constexpr int kLongMinWs = 8192;
 constexpr int kCandCap = 12288;    // survivors resolvable in LDS (96 KiB of key/index pairs)
 constexpr int kHistBins = 2048;    // 11-bit digits
 constexpr int kPassMax = 3;        // range-relative 11-bit digits resolve 32-bit keys in 3 passes
@@ -384,7 +389,7 @@ __device__ void emit_selected(const Src& src, int m, const Threshold& th, SelSta
 __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
     RowHeader* __restrict__ hdr, uint32_t* __restrict__ counts, int max_chunks,
-    uint2* __restrict__ cand, const float* __restrict__ gsamp, int n_off) {
+    uint2* __restrict__ cand, const float* __restrict__ gsamp, int n_off, int long_min) {
   __shared__ uint32_t samp[kSample];
   __shared__ __attribute__((aligned(16))) int hist[kPassMax * kHistBins];
   __shared__ SelState st;
@@ -397,7 +402,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
   int64_t n64 = (int64_t)n_valid[r] + n_off;
   n64 = n64 < 0 ? 0 : (n64 > ld ? ld : n64);
   const int n = (int)n64;
-  if (n <= kRowMax || n <= k) return;
+  if (n <= long_min || n <= k) return;
   const int nch = (n + kChunk - 1) / kChunk;
   if (c >= nch) return;
   const float* row = scores + (int64_t)r * ld;
@@ -795,7 +800,7 @@ __device__ void resolve_long_row(const float* __restrict__ row, int ld, int n, i
 __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
     int32_t* __restrict__ idx, const RowHeader* __restrict__ hdr, const uint32_t* __restrict__ counts,
-    int max_chunks, const uint2* __restrict__ cand, int n_off) {
+    int max_chunks, const uint2* __restrict__ cand, int n_off, int long_min) {
   static_assert(kRowThreads == kResolveThreads, "one kernel serves both paths");
   extern __shared__ uint32_t smem[];  // long rows: survivor keys, ids and chunk offsets
   __shared__ __attribute__((aligned(16))) int hist[kPassMax * kHistBins];
@@ -811,7 +816,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     for (int i = threadIdx.x; i < k; i += kRowThreads) out[i] = i < n ? i : -1;
     return;
   }
-  if (n <= kRowMax) {
+  if (n <= long_min) {
     if (n <= kRowMax / 4) select_mid_row<kRowMax / 4 / kRowThreads>(row, n, k, out, hist, st);
     else if (n <= kRowMax / 2) select_mid_row<kRowMax / 2 / kRowThreads>(row, n, k, out, hist, st);
     else select_mid_row<kRowMax / kRowThreads>(row, n, k, out, hist, st);
@@ -839,7 +844,7 @@ WsLayout ws_layout(int R, int64_t ld) {
 
 }  // namespace
 
-int topk_long_row_min() { return kRowMax; }
+int topk_long_row_min(int64_t ld) { return ld > kRowMax ? kLongMinWs : kRowMax; }
 
 bool topk_shape_ok(int R, int64_t ld) {
   return (int64_t)R * ws_layout(1, ld).max_chunks <= 2147483647LL;
@@ -853,20 +858,21 @@ size_t topk_workspace_bytes(int R, int64_t ld, int k) {
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
                        int32_t* idx, void* ws, hipStream_t s, const float* samp, int n_off) {
   const WsLayout L = ws_layout(R, ld);
+  const int long_min = topk_long_row_min(ld);
   char* wsb = static_cast<char*>(ws);
   RowHeader* hdr = L.total ? reinterpret_cast<RowHeader*>(wsb + L.hdr) : nullptr;
   uint32_t* counts = L.total ? reinterpret_cast<uint32_t*>(wsb + L.counts) : nullptr;
   uint2* cand = L.total ? reinterpret_cast<uint2*>(wsb + L.cand) : nullptr;
   if (L.total) {
     topk_prep_kernel<<<(unsigned)R * (unsigned)L.max_chunks, kLongThreads, 0, s>>>(
-        scores, ld, n_valid, k, hdr, counts, L.max_chunks, cand, samp, n_off);
+        scores, ld, n_valid, k, hdr, counts, L.max_chunks, cand, samp, n_off, long_min);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // Long rows: survivor keys and ids, then the chunk offsets (rows up to kRowMax need none).
   const size_t lds = L.total ? sizeof(uint32_t) * (2 * (size_t)kCandCap + L.max_chunks + 1) : 0;
   topk_finish_kernel<<<R, kRowThreads, lds, s>>>(
-      scores, ld, n_valid, k, idx, hdr, counts, L.max_chunks, cand, n_off);
+      scores, ld, n_valid, k, idx, hdr, counts, L.max_chunks, cand, n_off, long_min);
   return hipGetLastError();
 }
 
