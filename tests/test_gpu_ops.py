@@ -138,7 +138,9 @@ def test_index_topk_equals_the_two_calls(paged):
     two rows are also checked against the oracle's top-k under the band rule."""
     import long_context_sparse_06_amd as dsa
     _case(f"index_topk paged={paged}")
-    lengths = np.array([70000, 33000, 40000, 5000, 1500, 2049, 50000, 45000, 131072])
+    # rows 9..12: 8192 (one workgroup's register select) and 8193..32768 (compaction, since
+    # the call's capacity exceeds 32768)
+    lengths = np.array([70000, 33000, 40000, 5000, 1500, 2049, 50000, 45000, 131072, 8192, 8193, 20000, 32768])
     inp = datagen.make_decode(len(lengths), None, FULL, seed=51, lengths=lengths, paged=paged)
 
     def slot(b, s):  # storage index of token s of sequence b in k_scale
@@ -402,6 +404,21 @@ def test_topk_long_rows_exact():
     _expect_topk(s, n_valid, k, got)
     got2 = _run_topk(s, n_valid, k)                        # workspace reuse, determinism
     assert np.array_equal(got, got2)
+
+
+def test_topk_rows_routed_to_compaction():
+    """With a leading dimension above 32768 (so the compaction workspace exists), rows of
+    8193..32768 scores take the sampled compaction rather than the register select; 8192 and
+    shorter stay in one workgroup.  Includes coarse values (ties at the threshold)."""
+    _case("topk rows of 8k..32k with the compaction workspace")
+    rng = np.random.default_rng(38)
+    ld, k = 65536, 2048
+    n_valid = [8192, 8193, 9000, 12288, 16384, 20000, 32767, 32768, 65536, 4097]
+    s = rng.standard_normal((len(n_valid), ld)).astype(np.float32)
+    s[3] = np.round(s[3] * 8) / 8                          # coarse: ties at the threshold
+    s[6] = np.round(s[6] * 64) / 64
+    got = _run_topk(s, n_valid, k)
+    _expect_topk(s, n_valid, k, got)
 
 
 def test_topk_long_rows_sample_misses_survivors():
