@@ -222,6 +222,7 @@ class PrefillInputs:
                   q_scale / k_scale are all ones.
     fp8/bf16 ("mixed"): q_idx e4m3 codes with per-token scale [T], keys e4m3 codes
                   with per-token scale [T], q / kv bf16 bits.
+    needles [n] (peaked regime only): the planted token positions.
     """
     shapes: Shapes
     T: int
@@ -233,23 +234,47 @@ class PrefillInputs:
     k_scale: np.ndarray
     q: np.ndarray
     kv: np.ndarray
+    needles: Optional[np.ndarray] = None
 
 
-def make_prefill(T: int, shapes: Shapes = FULL, seed: int = 0, dtype: str = "mixed") -> PrefillInputs:
+def make_prefill(T: int, shapes: Shapes = FULL, seed: int = 0, dtype: str = "mixed",
+                 regime: str = "gaussian", n_needles: int = 16) -> PrefillInputs:
+    """Synthetic causal-prefill inputs.
+
+    regime="gaussian": the configurations' N(0,1)/sqrt(d) activations.
+    regime="peaked": unscaled N(0,1) q and latent rows, and `n_needles` planted token
+    positions.  Every indexer query head gets 0.5 * a added and each needle key 4 * a (a a
+    random unit vector), so a needle's per-head dots are about 2 against ~0.1 for other
+    tokens and every row at or after a needle keeps it; every query head gets 0.3 * c added
+    and each needle latent row 0.7 * c (c with N(0,1) coordinates), which lifts a needle's
+    logit by about 0.21 * 576 / 24 = 5 at the 1/sqrt(576) scale, so attention is far from
+    uniform.
+    """
     rng = np.random.default_rng(seed)
     s = shapes
+    unscaled = regime == "peaked"
     qi = gaussian(rng, (T, s.HI, s.dI))
     w = rng.uniform(0.0, 1.0, size=(T, s.HI)).astype(np.float32)
     ki = gaussian(rng, (T, s.dI))
-    q = gaussian(rng, (T, s.H, s.Dqk))
-    kv = gaussian(rng, (T, s.Dqk))
+    q = gaussian(rng, (T, s.H, s.Dqk), unscaled=unscaled)
+    kv = gaussian(rng, (T, s.Dqk), unscaled=unscaled)
+    needles = None
+    if regime == "peaked":
+        needles = np.sort(rng.choice(T, size=min(n_needles, T), replace=False)).astype(np.int64)
+        a = rng.standard_normal(s.dI).astype(np.float32)
+        a /= np.float32(np.linalg.norm(a))
+        c = rng.standard_normal(s.Dqk).astype(np.float32)
+        qi += np.float32(0.5) * a
+        ki[needles] += np.float32(4.0) * a
+        q += np.float32(0.3) * c
+        kv[needles] += np.float32(0.7) * c
     if dtype == "f32":
         ones = np.ones(T, dtype=np.float32)
-        return PrefillInputs(s, T, "f32", qi, ones, w, ki, ones.copy(), q, kv)
+        return PrefillInputs(s, T, "f32", qi, ones, w, ki, ones.copy(), q, kv, needles)
     q_codes, q_scale = quantize_e4m3_per_token(qi.reshape(T, -1))
     k_codes, k_scale = quantize_e4m3_per_token(ki)
     return PrefillInputs(s, T, "mixed", q_codes.reshape(T, s.HI, s.dI), q_scale, w,
-                         k_codes, k_scale, to_bf16_bits(q), to_bf16_bits(kv))
+                         k_codes, k_scale, to_bf16_bits(q), to_bf16_bits(kv), needles)
 
 
 def make_config(config: int, **over):
@@ -257,7 +282,8 @@ def make_config(config: int, **over):
     c = CONFIGS[config]
     seed = over.pop("seed", seed_for(config))
     if c["kind"] == "prefill":
-        return make_prefill(over.pop("T", c["T"]), c["shapes"], seed, "f32" if c.get("dtype") == "f32" else "mixed")
+        return make_prefill(over.pop("T", c["T"]), c["shapes"], seed,
+                            "f32" if c.get("dtype") == "f32" else "mixed", **over)
     if c.get("paged"):
         rng = np.random.default_rng(seed + 7)
         B = over.pop("B", c["B"])

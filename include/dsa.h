@@ -49,7 +49,8 @@ typedef enum {
   DSA_ERR_DTYPE = 3,       /* dtype not accepted by this entry point                   */
   DSA_ERR_WORKSPACE = 4,   /* workspace pointer NULL or smaller than required          */
   DSA_ERR_LAUNCH = 5,      /* the HIP runtime reported an error after launching        */
-  DSA_ERR_UNSUPPORTED = 6  /* valid but unsupported combination (e.g. page size % 16)  */
+  DSA_ERR_UNSUPPORTED = 6  /* valid but unsupported combination (e.g. an fp32 shape
+                              beyond the generic kernel's LDS)                         */
 } dsa_status;
 
 typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_E4M3 = 2 } dsa_dtype;
@@ -61,7 +62,8 @@ typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_E4M3 = 2 } dsa_dtype;
  *                                      + s % page_size) * D
  * D is the row width given to the call.  `scale` (indexer keys only) is the per-token
  * fp32 dequantisation scale with the same addressing and a width of one float; NULL
- * means 1.  Pages hold 64 tokens in the paged workloads (the pages do not fix a size).
+ * means 1.  Any page size >= 1 is accepted; the paged workloads use 64-token pages (the
+ * pages do not fix a size).
  */
 typedef struct {
   const void* data;
@@ -82,8 +84,8 @@ typedef struct {
  * for seq = row_seq[r] and every s in [0, n_r), n_r = row_pos[r] + 1 (the query's own
  * token is a candidate).  Entries s >= n_r of a score row are left untouched.
  *
- *   dt        DSA_E4M3: q and keys are e4m3 codes (fast path: H_I == 64, d_I == 128,
- *             paged page_size % 16 == 0); DSA_F32: q and keys are fp32 (any shape).
+ *   dt        DSA_E4M3: q and keys are e4m3 codes (fast path: H_I == 64, d_I == 128, any
+ *             page size); DSA_F32: q and keys are fp32 (any shape).
  *   q         [R, H_I, d_I]          q_scale [R] or NULL (= 1)     w [R, H_I] fp32
  *   keys      cache of rows of width d_I (+ per-token scale)
  *   row_seq   [R] int32 sequence of each row      row_pos [R] int32 position of each row

@@ -9,7 +9,8 @@
   score within 1e-3 relative of the oracle's k-th score tau.
 * Standalone top-k on identical fp32 inputs: bit-exact.
 * Attention output vs the oracle evaluated on the GPU's own kept set: max-abs <= 2e-2
-  (bf16 path) or <= 1e-4 (fp32 path).
+  (bf16 path) or <= 1e-4 (fp32 path); the log-sum-exp to the same bound (its finiteness
+  must match exactly).
 """
 from __future__ import annotations
 
@@ -66,7 +67,7 @@ def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, atol, what=""):
     assert np.array_equal(np.isfinite(lse_gpu), fin), f"{what}: lse finiteness differs"
     if fin.any():
         lerr = np.abs(np.asarray(lse_gpu, dtype=np.float64)[fin] - lse_ref[fin]).max()
-        assert lerr <= max(atol, 1e-3), f"{what}: lse max-abs {lerr:.3e}"
+        assert lerr <= atol, f"{what}: lse max-abs {lerr:.3e}"
     return err
 
 

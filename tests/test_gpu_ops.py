@@ -368,13 +368,17 @@ def test_topk_lds_row_max_and_small_k():
         _expect_topk(s, [32768, 32768, 20000], k, got)
 
 
-def test_topk_mid_rows_sampled_and_fallback():
-    """Rows of 12289..32768 scores take a sample threshold before compaction; all-equal and
-    coarse rows overflow the survivor list and fall back to the full row; a row whose largest
-    scores sit on half the sampled positions keeps fewer than k survivors and falls back too."""
-    _case("topk mid rows")
+@pytest.mark.parametrize("ld", [32768, 65536])
+def test_topk_mid_rows_sampled_and_fallback(ld):
+    """Rows of 12288..32768 scores.  With ld = 32768 the call has no compaction workspace and
+    every row is selected in registers by one workgroup (multi-pass radix select).  With
+    ld = 65536 the same rows (longer than 8192) take the sampled compaction: all-equal and
+    coarse rows overflow the survivor list and fall back to the full row, and a row whose
+    largest scores sit on half the sampled positions keeps fewer than k survivors and falls
+    back too."""
+    _case(f"topk mid rows ld={ld}")
     rng = np.random.default_rng(35)
-    ld, k = 32768, 2048
+    k = 2048
     n_valid = [32768, 12289, 20000, 32768, 30000, 32768, 16000, 12288, 25000]
     R = len(n_valid)
     s = rng.standard_normal((R, ld)).astype(np.float32)
