@@ -146,6 +146,28 @@ dsa_status dsa_sparse_mla_decode(dsa_dtype dt, const void* q, const dsa_cache* k
                                  size_t ws_bytes, hipStream_t stream);
 
 /*
+ * dsa_sparse_mla_decode_noalloc -- dsa_sparse_mla_decode for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without a workspace, the same kernels and the same result bit for bit.  The
+ * split-KV partials go to a static device array of dsa_noalloc_scratch_bytes() bytes (32 MiB),
+ * one per GPU, held until the process ends.  It calls no allocator.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, or two threads without ordering) race and give undefined results; serialise them.
+ * The array keeps the last call's contents; nothing in it needs clearing (every partial a
+ * call reads is written by the same call first).
+ * Errors: as dsa_sparse_mla_decode, plus DSA_ERR_WORKSPACE when the partials this call needs
+ * (dsa_sparse_mla_decode_workspace_size) exceed the array, and DSA_ERR_LAUNCH when the
+ * array's device address cannot be looked up.  The lookup runs once per device, on the
+ * first call with that device current.
+ */
+size_t dsa_noalloc_scratch_bytes(void);
+dsa_status dsa_sparse_mla_decode_noalloc(dsa_dtype dt, const void* q, const dsa_cache* kv,
+                                         const int32_t* idx, int B, int H, int Dqk, int Dv, int k,
+                                         float softmax_scale, void* out, float* lse,
+                                         hipStream_t stream);
+
+/*
  * dsa_sparse_mla_prefill -- the same attention for every token t of one sequence,
  * each over its own kept set S_t = { idx[t, j] >= 0 } (causal selection is the
  * caller's: dsa_topk with n_valid[t] = t + 1 keeps only s <= t).

@@ -20,7 +20,7 @@ __all__ = [
     "dsa_sparse_mla_decode_workspace_size", "dsa_sparse_mla_prefill", "dsa_masked_mla_prefill",
     "dsa_index_topk", "dsa_index_topk_workspace_size", "dsa_indexer_quality",
     "dsa_indexer_quality_workspace_size",
-    "dsa_cache_append",
+    "dsa_cache_append", "dsa_sparse_mla_decode_noalloc", "dsa_noalloc_scratch_bytes",
     "dsa_status_string", "exported_symbols",
 ]
 
@@ -70,6 +70,9 @@ _SIGS = {
                                       _vp, _vp]),
     "dsa_cache_append": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, ctypes.POINTER(_Cache),
                                 ctypes.POINTER(_Cache), _vp]),
+    "dsa_noalloc_scratch_bytes": (_sz, []),
+    "dsa_sparse_mla_decode_noalloc": (_i32, [_i32, _vp, ctypes.POINTER(_Cache), _vp, _i32, _i32, _i32,
+                                             _i32, _i32, _f32, _vp, _vp, _vp]),
     "dsa_status_string": (ctypes.c_char_p, [_i32]),
 }
 
@@ -171,6 +174,20 @@ def dsa_sparse_mla_decode(dt: int, q, kv: Cache, idx, B: int, H: int, Dqk: int, 
     _check("dsa_sparse_mla_decode", lib().dsa_sparse_mla_decode(
         dt, _ptr(q), ctypes.byref(c), _ptr(idx), B, H, Dqk, Dv, k, softmax_scale, _ptr(out),
         _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dsa_noalloc_scratch_bytes() -> int:
+    return int(lib().dsa_noalloc_scratch_bytes())
+
+
+def dsa_sparse_mla_decode_noalloc(dt: int, q, kv: Cache, idx, B: int, H: int, Dqk: int, Dv: int,
+                                  k: int, softmax_scale: float, out, lse=None, stream=None):
+    """dsa_sparse_mla_decode with its split partials in the library's static per-GPU array
+    (no workspace, no allocation; overlapping calls on one GPU race)."""
+    c = kv._c()
+    _check("dsa_sparse_mla_decode_noalloc", lib().dsa_sparse_mla_decode_noalloc(
+        dt, _ptr(q), ctypes.byref(c), _ptr(idx), B, H, Dqk, Dv, k, softmax_scale, _ptr(out),
+        _ptr(lse), _stream(stream)))
 
 
 def dsa_sparse_mla_prefill(dt: int, q, kv, idx, T: int, H: int, Dqk: int, Dv: int, k: int,

@@ -85,6 +85,13 @@ def test_host_validation_paths():
     assert L.dsa_sparse_mla_decode_workspace_size(128, 128, 512, 2048) == 0       # one split
     assert L.dsa_sparse_mla_decode_workspace_size(128, 128, 512, 16384) == 128 * 2 * 128 * part
     assert L.dsa_sparse_mla_decode_workspace_size(512, 128, 512, 9000) == 512 * 2 * 128 * part
+    # the no-allocation decode: same validation, plus the static array's size limit (checked on
+    # the host before the array is looked up)
+    assert L.dsa_noalloc_scratch_bytes() == 32 << 20
+    assert L.dsa_sparse_mla_decode_noalloc(dsa.BF16, None, ctypes.byref(kv), FAKE, 8, 128, 576, 512, 2048, 0.04, FAKE, None, None) == 1
+    assert L.dsa_sparse_mla_decode_noalloc(dsa.BF16, FAKE, ctypes.byref(kv), FAKE, 0, 128, 576, 512, 2048, 0.04, FAKE, None, None) == 2
+    assert L.dsa_sparse_mla_decode_workspace_size(128, 128, 512, 16384) > L.dsa_noalloc_scratch_bytes()
+    assert L.dsa_sparse_mla_decode_noalloc(dsa.BF16, FAKE, ctypes.byref(kv), FAKE, 128, 128, 576, 512, 16384, 0.04, FAKE, None, None) == 4
     # fused index + top-k
     fw = L.dsa_index_topk_workspace_size(4, 131072, 2048)
     assert fw > 4 * 131072 * 4
