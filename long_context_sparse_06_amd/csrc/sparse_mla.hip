@@ -30,6 +30,8 @@
 namespace dsa {
 namespace {
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kTok = 32;                        // rows per LDS tile
@@ -47,6 +49,7 @@ constexpr int kMlaWaves = 8;                    // compute waves: two per 16-hea
 constexpr int kMlaThreads = (kMlaWaves + 1) * WAVE;  // + one copy wave
 constexpr int kHeadsPerWg = 64;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleLog2 = 64.0f;  // wide kernel: largest lead of a logit over its reference max
 
 // Byte offset of (row, 16-byte chunk c) inside a tile.
 __device__ __forceinline__ int tile_off(int row, int c) {
@@ -110,6 +113,27 @@ template <int S>
 struct Slot {
   static constexpr int value = S;
 };
+// One wide LDS-DMA copy: every lane loads 16 bytes from its global address and the wave's
+// 64 pieces land contiguously at LDS byte address `lds` (M0) + 16 * lane.  Written as asm so
+// the compiler's wait-count pass, which cannot tell a ring slot being filled from one being
+// read, does not make every LDS read wait for every copy in flight; the caller orders copies
+// and reads itself (s_waitcnt vmcnt + barrier).  No VGPR is written.  M0 is a reserved
+// register the compiler does not let asm clobber; the kernels that use this copy make no
+// other use of M0 (a CPU test compiles them and checks the generated code).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory");
+}
+typedef __attribute__((address_space(3))) char lds_char;
+// The same slot as an LDS-address-space pointer: an address-space cast of the variable itself
+// (folded by the compiler, no null check), so alias analysis still sees which slot a read uses
+// and the wait-count pass does not make it wait for copies into the other slots.
+template <int S>
+__device__ __forceinline__ lds_char* ring_lds() {
+  return (lds_char*)ring_slot<S>();
+}
 
 // One workgroup = (row r, 64 heads, a range of the kept set): eight compute waves and one
 // copy wave.  Compute waves w and w+4 share head block w&3 (16 heads): for S^T = K Q^T each
@@ -451,6 +475,415 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   }
 }
 
+// Wide variant: one workgroup = (row, 32 * NW heads, a range of the kept set), NW waves and no
+// copy wave.  Per 32-row tile:
+//   * logits: wave w owns 32 heads over all 576 latent columns: S^T (32 tokens x 32 heads)
+//     = K Q^T with v_mfma_f32_32x32x16_bf16 (36 k-steps, one accumulation chain), so its
+//     logits need no exchange.  Softmax statistics of those heads live in wave w only.
+//   * P exchange: the 32x32 result layout leaves each lane 16 tokens of one head, which are
+//     exactly the B operand (P^T, two 16-token k-steps) of the value product; each wave
+//     publishes its heads' bf16 probabilities in LDS (2 KB); one barrier.
+//   * values: wave w accumulates O^T for ALL heads of the workgroup over its 512 / NW value
+//     columns (32x32x16 tiles), so each transposing V^T read from LDS feeds NW MFMAs and a
+//     tile's V^T crosses LDS once in total.
+// One wave issues 32x32x16 bf16 MFMAs at about 2.1 PFLOP/s chip-wide against about 1.4 for
+// 16x16x32 (own measurement, one wave per SIMD), hence this shape.  The accumulators (NW head
+// blocks x 16 / NW value blocks x 16 = 256 per lane) sit in AGPRs and the 32 heads' query
+// fragments in 144 VGPRs: one wave per SIMD.
+//
+// Tile layout in LDS (this variant): 36 blocks of 1 KB; block b holds rows 16 * (b & 1) .. + 15
+// and 16-byte chunks 4 * (b >> 1) .. + 3 of those rows, chunk-major with a row swizzle: chunk
+// cc of row rr at byte 256 * cc + 16 * (rr ^ 4 * cc).  One wide LDS-DMA copy fills one block
+// (lane l loads chunk l >> 4 of row (l & 15) ^ 4 * (l >> 4)), so a copy touches 16 rows'
+// 64-byte pieces -- 16 cache lines rather than the 64 of a copy taking 16 bytes from each of
+// 64 rows, which the memory path handles several times slower.  The swizzle makes both the K
+// fragment reads (16 rows of one chunk per 16 lanes) and the transposing V^T reads (4 rows x 2
+// chunks per 16 lanes) cover every LDS bank evenly: neither has bank conflicts.
+//
+// Gathers: every wave issues its share (36 / NW) of each tile's copies -- all in the same
+// 16-row half -- into a three-slot ring, two tiles ahead, spread over the logit MFMAs; the
+// first barrier of a tile both publishes tile t (each wave first waits for its own copies of
+// it) and retires tile t - 1, whose slot then takes tile t + 2.  The row list (cache row of
+// each kept token, -1 for none) and each tile's live-token mask are built by all waves before
+// the first copy.
+template <int NW, bool PAGED, bool SPLIT, bool MASKED = false>
+__global__ __launch_bounds__(NW * WAVE) void mla_wide_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ table, int max_pages, int page_size, int64_t seq_stride,
+    const int32_t* __restrict__ idx, int k, int H, int decode, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
+    float* __restrict__ part_ml, int n_split, int tok_per_split) {
+  static_assert(NW == 2 || NW == 4, "32 heads per wave, 64 or 128 per workgroup");
+  constexpr int HPW = 32 * NW;              // heads per workgroup
+  constexpr int CPW = kDmaPerTile / NW;     // copies per wave per tile
+  constexpr int KS = kDqk / 16;             // 36 k-steps of 16 latent columns
+  constexpr int CB = kDv / 32 / NW;         // 32-column value blocks per wave
+  extern __shared__ int srow[];  // [tok_per_split] cache row of each kept token (-1 = none),
+                                 // then [tiles] live-token mask of each tile (MASKED: masks only)
+  __shared__ int s_last[NW];
+  __shared__ __attribute__((aligned(16))) v8bf s_p[NW][2][WAVE];  // P^T fragments per head block
+  __shared__ float s_alpha[NW][32];                                // rescale factor per head
+  __shared__ int s_flag[2];                                        // a head rescaled (parity)
+  __shared__ float s_fin[NW][32];                                  // 1 / sum per head (epilogue)
+  const int HG = H / HPW;
+  int unit, hg;
+  {
+    const int b = (int)blockIdx.x, full = ((int)gridDim.x / HG) / 8 * 8 * HG;
+    if (b < full) {
+      unit = b / (8 * HG) * 8 + b % 8;
+      hg = (b / 8) % HG;
+    } else {
+      unit = full / HG + (b - full) / HG;
+      hg = (b - full) % HG;
+    }
+  }
+  const int sp = unit % n_split;
+  const int r = unit / n_split;
+  const int t_begin = MASKED ? 0 : sp * tok_per_split;
+  const int t_end = MASKED ? r + 1 : min(k, t_begin + tok_per_split);
+  const int n_tok = t_end > t_begin ? t_end - t_begin : 0;
+  const int ntiles = (n_tok + kTok - 1) / kTok;
+  const int seq = decode ? r : 0;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);  // wave-uniform (scalar)
+  const int n = lane & 31, h = lane >> 5;  // 32x32 MFMA lane coordinates
+  uint32_t* smask = reinterpret_cast<uint32_t*>(MASKED ? srow : srow + tok_per_split);
+
+  // ---- query fragments (B operand of S^T = K Q^T): lane (n, h) holds, for k-step ks,
+  // q[r, head n of this wave, 16 * ks + 8 * h .. + 7].  Issued first so their latency
+  // overlaps the row list.
+  v8bf qf[KS];
+  {
+    const int hd = hg * HPW + 32 * w + n;
+    const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)r * H + hd) * kDqk + 8 * h);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(v8bf, qp[2 * ks]);
+  }
+
+  // ---- row list and live masks
+  const uint16_t* base = PAGED ? kv : kv + (int64_t)seq * seq_stride * kDqk;
+  const uint16_t* dummy = q + (int64_t)r * H * kDqk;  // finite stand-in for dead rows
+  int last = -1;                                      // last live token this wave saw
+  if (tid < 2) s_flag[tid] = 0;
+  if (tid < NW * 32) s_alpha[tid / 32][tid % 32] = 1.0f;
+  if (MASKED) {
+    for (int i = tid; i < ntiles; i += NW * WAVE) smask[i] = 0u;
+    __syncthreads();
+    const int32_t* krow = idx + (int64_t)r * k;
+    for (int j = tid; j < k; j += NW * WAVE) {
+      const int s = krow[j];
+      if (s >= 0 && s < n_tok) {
+        atomicOr(&smask[s >> 5], 1u << (s & 31));
+        last = max(last, s);
+      }
+    }
+  } else {
+    const int32_t* irow = idx + (int64_t)r * k + t_begin;
+    for (int i0 = 64 * w; i0 < n_tok; i0 += 64 * NW) {
+      const int i = i0 + lane;
+      const int v = i < n_tok ? irow[i] : -1;
+      int row = v;
+      if (PAGED && v >= 0) row = table[(int64_t)seq * max_pages + v / page_size] * page_size + v % page_size;
+      const uint64_t live = ballot(row >= 0);
+      if (live) last = i0 + 63 - (int)__builtin_clzll(live);
+      if (i < n_tok) srow[i] = row;
+      if (lane == 0) {
+        const int t0 = i0 / kTok;
+        if (t0 < ntiles) smask[t0] = (uint32_t)live;
+        if (t0 + 1 < ntiles) smask[t0 + 1] = (uint32_t)(live >> 32);
+      }
+    }
+  }
+  {
+    int m = last;
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+    if (lane == 0) s_last[w] = m;
+  }
+  __syncthreads();
+  int lst = -1;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) lst = max(lst, s_last[i]);
+  // tiles run: through the last kept token (at least one when the range is not empty, so an
+  // all-dead range still writes its zero output and -inf statistics)
+  const int nt = ntiles == 0 ? 0 : max(1, min(ntiles, (lst + kTok) / kTok));
+
+  // This wave's copies are blocks j = w + NW * c: all in row half w & 1 (NW is even).  Lane
+  // l loads chunk 4 * (j >> 1) + (l >> 4) of tile row 16 * (w & 1) + ((l & 15) ^ 4 * (l >> 4)).
+  const int crow = 16 * (w & 1) + ((lane & 15) ^ (4 * (lane >> 4)));
+  // Cache row of this lane's copy row in tile t; tiles past the last one and dead tokens
+  // use the finite dummy row (-1).
+  auto tile_row = [&](int t) {
+    const int tok = t * kTok + crow;
+    return (t < nt && tok < n_tok) ? (MASKED ? tok : srow[tok]) : -1;
+  };
+  auto row_src = [&](int row) {
+    return (row >= 0 ? base + (int64_t)row * kDqk : dummy) + 8 * (lane >> 4);
+  };
+  // Copy c (of this wave's CPW) of a tile into block j = w + NW * c of the slot.
+  auto copy = [&](auto slot, const uint16_t* src, int c) {
+    constexpr int S = decltype(slot)::value;
+    const int j = w + NW * c;
+    lds_dma16(src + 32 * (j >> 1), __builtin_amdgcn_readfirstlane(lds_offset(ring_slot<S>()) + j * kBlock));
+  };
+  auto issue = [&](auto slot, int t) {
+    const uint16_t* src = row_src(tile_row(t));
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) copy(slot, src, c);
+  };
+  // The query fragments have landed (they were issued before the index loads the row list
+  // waited for); waiting here tells the compiler so, and no wait inside the tile loop is
+  // left to count them among the copies in flight.
+  wait_vmcnt<0>();
+  // Every step issues a full tile of copies (tiles past the last one copy the dummy row into
+  // the free slot), so each wave always has exactly one tile of copies in flight behind the
+  // one it waits for.
+  if (nt > 0) {
+    issue(Slot<0>{}, 0);
+    issue(Slot<1>{}, 1);
+  }
+  int next_row = tile_row(2);  // copy row of the tile two ahead, read one step early
+
+  v16f acc[CB][NW];  // value block x head block; lane (n, h): columns 8 j + 4 h + i, head n
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int b = 0; b < NW; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[cb][b][e] = 0.0f;
+  float m_run = -INFINITY;  // reference max of head n (log2 domain)
+  float l_run = 0.0f;       // this lane's share of the running sum
+  // K fragment (A operand) of k-step ks: lane (n, h) = row n, chunk 2 ks + h -> block
+  // 2 (ks >> 1) + (n >> 4), chunk-in-block cc = 2 (ks & 1) + h, at 256 cc + 16 ((n & 15) ^ 4 cc).
+  int k_lane[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int cc = 2 * p + h;
+    k_lane[p] = (n >> 4) * kBlock + 256 * cc + 16 * ((n & 15) ^ (4 * cc));
+  }
+  // V^T fragment (A operand) of value block CBg, k-step ks': lane (n, h) = value column
+  // 32 CBg + n, tokens 16 ks' + 4 h + 0..3 (lo) and 16 ks' + 8 + 4 h + 0..3 (hi).  The
+  // transposing read: in 16-lane group g = lane >> 4, lane i points at token row
+  // 16 ks' + 4 (g >> 1) + (i >> 2) (+ 8 for hi), columns 16 (g & 1) + 4 (i & 3) .. + 3 of the
+  // block = chunk 4 CBg + cc, cc = 2 (g & 1) + (i & 3) / 2, byte 8 (i & 1).
+  int v_lane[2];
+  {
+    const int g = lane >> 4, i = lane & 15;
+    const int cc = 2 * (g & 1) + ((i & 3) >> 1);
+    const int rr = 4 * (g >> 1) + (i >> 2);
+    v_lane[0] = 256 * cc + 16 * (rr ^ (4 * cc)) + 8 * (i & 1);
+    v_lane[1] = 256 * cc + 16 * ((rr + 8) ^ (4 * cc)) + 8 * (i & 1);
+  }
+
+  auto step = [&](auto slot, int t) {
+    constexpr int S = decltype(slot)::value;
+    constexpr int SN = (S + 2) % kNBuf;
+    // This wave's copies of tile t landed (those of t + 1 may be in flight) and its LDS
+    // writes of the previous tile (flag clear, rescale factors) completed.
+    __builtin_amdgcn_s_waitcnt((CPW & 15) | (0 << 8) | (7 << 4) | ((CPW >> 4) << 14));
+    // Every wave's copies of tile t landed; tile t - 1 (and its P) retired.  A bare barrier: a
+    // workgroup fence here would also wait for tile t + 1's copies.  The empty asm keeps the
+    // compiler from moving LDS accesses across it.
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // Clear the other parity's rescale flag for tile t + 1: every wave read it at tile t - 1
+    // and has passed the barrier above since.
+    if (tid == 0) s_flag[(t + 1) & 1] = 0;
+    const uint16_t* nsrc = row_src(next_row);
+    const char* tb = ring_slot<S>();
+    const uint32_t live = smask[t];
+    // ---- S^T = K Q^T for the own 32 heads, one accumulation chain (a second chain's 16
+    // registers push query fragments out of registers and costs more than it gains).  Tile
+    // t + 2's copies go out one every KS / CPW k-steps, behind the MFMAs.
+    constexpr int KD = 3;
+    constexpr int CSTEP = KS / CPW;
+    auto kfrag = [&](int ks) {
+      return *reinterpret_cast<const v8bf*>(tb + (ks >> 1) * 2 * kBlock + k_lane[ks & 1]);
+    };
+    v8bf kf[KD];
+#pragma unroll
+    for (int i = 0; i < KD; ++i) kf[i] = kfrag(i);
+    v16f sc[1];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[0][e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const v8bf a = kf[ks % KD];
+      if (ks + KD < KS) kf[ks % KD] = kfrag(ks + KD);
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc[0], 0, 0, 0);
+      if (ks % CSTEP == 0 && ks / CSTEP < CPW) copy(Slot<SN>{}, nsrc, ks / CSTEP);
+    }
+    // ---- online softmax of head n: register 4 j + i holds token 8 j + 4 h + i
+    // Dead tokens' logits become -inf (their probability exp2(-inf) = 0); a fully live tile
+    // (the usual case; uniform) skips the per-token test.
+    if (live != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (!((live >> (8 * (e >> 2) + 4 * h + (e & 3))) & 1u)) sc[0][e] = -INFINITY;
+    }
+    float mx = -INFINITY;  // this lane's max scaled logit (the head's max needs lane n + 32 too)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[0][e]);
+    mx *= scale_log2;  // scale_log2 > 0
+    // Reference max: the first tile with a live token sets it (the accumulators are still
+    // zero); afterwards it moves only when a logit exceeds it by more than 2^64 (log2 domain),
+    // so p <= 2^64 and sums of 2^13 such terms stay far inside the fp32 and bf16 ranges.  Such
+    // a move (rare) rescales every wave's accumulators of the head, through s_alpha; no VALU
+    // instruction otherwise takes an accumulator as an operand, so they stay in AGPRs.  Both
+    // lanes of a head hold the same reference, so testing each lane's own max finds every
+    // head that needs a move.
+    float m_ref = m_run;
+    float alpha = 1.0f;
+    bool resc = false;
+    if (__ballot(m_ref == -INFINITY)) {  // a head with no live token yet (first tiles only)
+      mx = max_x32(mx);
+      if (m_ref == -INFINITY) m_ref = mx;  // stays -inf while the head has no live token
+    } else if (__ballot(mx > m_ref + kRescaleLog2)) {
+      mx = max_x32(mx);
+      const float m_new = fmaxf(m_ref, mx);
+      alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
+      m_ref = m_new;
+      resc = true;
+    }
+    m_run = m_ref;
+    const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+    float psum = 0.0f;
+    v8bf pf[2];  // P^T of k-step ks': slot 8 h + e' <-> token 16 ks' + 8 (e' >> 2) + 4 h + (e' & 3)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[0][e], scale_log2, -m_use));
+      psum += p;
+      pf[e >> 3][e & 7] = (__bf16)p;
+    }
+    l_run += psum;
+    s_p[w][0][lane] = pf[0];
+    s_p[w][1][lane] = pf[1];
+    if (resc) {
+      if (h == 0) s_alpha[w][n] = alpha;
+      if (lane == 0) s_flag[t & 1] = 1;
+    }
+    next_row = tile_row(t + 3);  // for the next step's copies; its LDS latency hides here
+    // Every head's probabilities are in LDS: this wave's writes have completed (lgkmcnt(0);
+    // the bare barrier does not wait for them) before any wave passes the barrier.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (s_flag[t & 1]) {  // rare: some head's reference max moved; rescale its accumulators
+      volatile v16f tmp;
+#pragma unroll
+      for (int b = 0; b < NW; ++b) {
+        const float a = s_alpha[b][n];
+        if (__ballot(a != 1.0f)) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            tmp = acc[cb][b];
+            v16f x = tmp;
+            tmp = x * a;
+            acc[cb][b] = tmp;
+          }
+        }
+      }
+    }
+    // ---- O^T += V^T P^T over this wave's value blocks, every head block of the workgroup;
+    // one 16-token k-step at a time (half the P fragments live at once)
+    auto vfrag = [&](int cb, int ks2) {
+      lds_char* vb = ring_lds<S>() + (2 * (CB * w + cb) + ks2) * kBlock;
+      const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(vb + v_lane[0]));
+      const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(vb + v_lane[1]));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    constexpr int VD = 2;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      v8bf pb[NW];
+#pragma unroll
+      for (int b = 0; b < NW; ++b) pb[b] = s_p[b][ks2][lane];
+      v8bf vf[VD];
+#pragma unroll
+      for (int d = 0; d < VD; ++d) vf[d] = vfrag(d, ks2);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const v8bf a = vf[cb % VD];
+        if (cb + VD < CB) vf[cb % VD] = vfrag(cb + VD, ks2);
+#pragma unroll
+        for (int b = 0; b < NW; ++b)
+          acc[cb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[b], acc[cb][b], 0, 0, 0);
+      }
+    }
+    if (resc && h == 0) s_alpha[w][n] = 1.0f;
+  };
+  __syncthreads();  // the rescale factors and flags are set
+
+  for (int t = 0; t < nt; t += kNBuf) {
+    step(Slot<0>{}, t);
+    if (t + 1 < nt) step(Slot<1>{}, t + 1);
+    if (t + 2 < nt) step(Slot<2>{}, t + 2);
+  }
+  wait_vmcnt<0>();  // the copies issued past the last tile land before the LDS is released
+
+  // ---- epilogue: statistics of the own heads, then every wave's value columns of all heads
+  {
+    const int hd = hg * HPW + 32 * w + n;
+    const float l = sum_x32(l_run);
+    if (h == 0) {
+      s_fin[w][n] = l > 0.0f ? 1.0f / l : 0.0f;
+      if (SPLIT) {
+        const int64_t pr = ((int64_t)r * n_split + sp) * H + hd;
+        part_ml[2 * pr] = m_run;
+        part_ml[2 * pr + 1] = l;
+      } else if (lse) {
+        lse[(int64_t)r * H + hd] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+      }
+    }
+  }
+  // The output (or this split's partial) rows go out through LDS: every wave scales its
+  // accumulators and writes them as bf16 into the (now idle) ring, rows padded to 1040 bytes,
+  // then each store instruction writes one head's whole 1 KB row.  Storing straight from the
+  // accumulator layout would spread every instruction's 8-byte pieces over 32 head rows.
+  // Two rounds of HPW / 2 heads (66.5 KB each) fit in the ring.
+  __syncthreads();  // s_fin visible; every wave is done with the ring
+  constexpr int RH = HPW / 2;            // head rows per round
+  constexpr int ROWB = kDv * 2 + 16;     // padded LDS row: 2-way bank conflicts at most
+  static_assert(RH * ROWB <= kNBuf * kBufBytes, "staging fits in the ring");
+  // byte o of the staging area: the ring's slots are separate variables, so o is split into
+  // a slot and an offset (rows never straddle a slot: ROWB-aligned rows are placed per slot)
+  constexpr int RPS = kBufBytes / ROWB;  // rows per slot
+  static_assert((RH + RPS - 1) / RPS <= kNBuf, "rows fit the slots");
+  auto stage_ptr = [&](int o) -> char* {
+    const int row = o / ROWB, off = o - row * ROWB;
+    const int sl = row / RPS, rs = row - sl * RPS;
+    char* base = sl == 0 ? g_ring0 : (sl == 1 ? g_ring1 : g_ring2);
+    return base + rs * ROWB + off;
+  };
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+#pragma unroll
+    for (int bb = 0; bb < NW / 2; ++bb) {
+      const int b = rd * (NW / 2) + bb;
+      const float inv = s_fin[b][n];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const v16f& x = acc[cb][b];
+          const uint32_t lo = f32_to_bf16(x[4 * j] * inv) | ((uint32_t)f32_to_bf16(x[4 * j + 1] * inv) << 16);
+          const uint32_t hi = f32_to_bf16(x[4 * j + 2] * inv) | ((uint32_t)f32_to_bf16(x[4 * j + 3] * inv) << 16);
+          const int row = 32 * bb + n, c = 32 * CB * w + 32 * cb + 8 * j + 4 * h;
+          *reinterpret_cast<uint2*>(stage_ptr(row * ROWB + 2 * c)) = make_uint2(lo, hi);
+        }
+    }
+    __syncthreads();
+    for (int row = w; row < RH; row += NW) {
+      const int hd = hg * HPW + rd * RH + row;
+      uint16_t* dst = SPLIT ? part_o + (((int64_t)r * n_split + sp) * H + hd) * kDv
+                            : out + ((int64_t)r * H + hd) * kDv;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage_ptr(row * ROWB + 16 * lane));
+      *reinterpret_cast<uint4*>(dst + 8 * lane) = v;
+    }
+    if (rd == 0) __syncthreads();  // round 0's rows are read before round 1 overwrites them
+  }
+}
+
 // Log-sum-exp merge of the split partials: one wave per (row, head), 8 value columns per
 // lane (16-byte loads and stores).  Split s contributes its normalized output u_s with
 // weight l_s * 2^(m_s - M).  Splits are taken NB at a time (NB = the split count rounded up
@@ -605,13 +1038,86 @@ SplitPlan split_plan(int B, int H, int k) {
   return {ns, tps};
 }
 
+hipError_t launch_combine(const uint16_t* part_o, const float* part_ml, int R, int H, int n_split,
+                          uint16_t* out, float* lse, hipStream_t s) {
+  const int RH = R * H;
+  const unsigned cgrid = (unsigned)((RH + kCombinePairs - 1) / kCombinePairs);
+  if (n_split <= 2)
+    mla_combine_kernel<2><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, n_split, out, lse);
+  else if (n_split <= 4)
+    mla_combine_kernel<4><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, n_split, out, lse);
+  else if (n_split <= 8)
+    mla_combine_kernel<8><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, n_split, out, lse);
+  else
+    mla_combine_kernel<16><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, n_split, out, lse);
+  return hipGetLastError();
+}
+
+// Decode dispatch.  The wide kernel (128 heads per workgroup) processes a tile with fewer,
+// larger MFMAs but carries more fixed cost per workgroup (query fragments of 128 heads, 128
+// KB of output or partials); it wins once the batch alone gives many (row, 128-head) groups,
+// so every split holds many tiles.  Below that the 64-head kernel, whose workgroups start and
+// finish faster, is quicker (measured at 8 x 131072 and 32 x 8192 against 64 x 20000).
+constexpr int kWideMinGroups = 64;
+
+bool decode_wide(int B, int H) { return H % 128 == 0 && B * (H / 128) >= kWideMinGroups; }
+
+// Waves (32 heads each) per workgroup of the wide kernel.
+int wide_nw(int H) { return H % 128 == 0 ? 4 : 2; }
+
+SplitPlan split_plan_wide(int B, int H, int k) {
+  // ~256 workgroups (one per CU: the ring leaves no LDS for a second), at least 4 tiles and
+  // at most kMaxTokPerWg kept tokens per workgroup
+  const int groups = B * (H / (32 * wide_nw(H)));
+  int ns = (256 + groups - 1) / groups;
+  const int max_ns = (k + 4 * kTok - 1) / (4 * kTok);
+  ns = ns < 1 ? 1 : (ns > max_ns ? max_ns : ns);
+  const int min_ns = (k + kMaxTokPerWg - 1) / kMaxTokPerWg;
+  ns = ns < min_ns ? min_ns : ns;
+  int tps = (k + ns - 1) / ns;
+  tps = (tps + kTok - 1) / kTok * kTok;
+  ns = (k + tps - 1) / tps;
+  return {ns, tps};
+}
+
+SplitPlan decode_plan(int B, int H, int k) {
+  return decode_wide(B, H) ? split_plan_wide(B, H, k) : split_plan(B, H, k);
+}
+
+template <int NW>
+hipError_t launch_wide(const uint16_t* q, const CacheView& kv, const int32_t* idx, int R, int H,
+                       int k, bool decode, bool masked, float scale_log2, uint16_t* out, float* lse,
+                       uint16_t* part_o, float* part_ml, SplitPlan p, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)R * (H / (32 * NW)) * p.n_split);
+  const uint16_t* kvp = static_cast<const uint16_t*>(kv.data);
+  if (masked) {
+    const size_t lds = sizeof(uint32_t) * (size_t)((R + kTok - 1) / kTok);
+    mla_wide_kernel<NW, false, false, true><<<grid, NW * WAVE, lds, s>>>(
+        q, kvp, nullptr, 0, 1, (int64_t)R, idx, k, H, 0, scale_log2, out, lse, nullptr, nullptr, 1, 0);
+    return hipGetLastError();
+  }
+  const size_t lds = mla_lds_bytes(p.tok_per_split);
+#define DSA_WIDE_LAUNCH(PG, SP)                                                                   \
+  mla_wide_kernel<NW, PG, SP><<<grid, NW * WAVE, lds, s>>>(q, kvp, kv.table, kv.max_pages,          \
+                                                           kv.page_size, kv.seq_stride, idx, k, H,   \
+                                                           decode ? 1 : 0, scale_log2, out, lse,     \
+                                                           part_o, part_ml, p.n_split, p.tok_per_split)
+  if (kv.table) {
+    if (p.n_split > 1) DSA_WIDE_LAUNCH(true, true); else DSA_WIDE_LAUNCH(true, false);
+  } else {
+    if (p.n_split > 1) DSA_WIDE_LAUNCH(false, true); else DSA_WIDE_LAUNCH(false, false);
+  }
+#undef DSA_WIDE_LAUNCH
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int mla_max_tokens_per_wg() { return kMaxTokPerWg; }
 
 size_t mla_decode_workspace_bytes(int B, int H, int Dv, int k) {
   if (Dv != kDv || H % kHeadsPerWg != 0) return 0;  // generic path needs no workspace
-  const SplitPlan p = split_plan(B, H, k);
+  const SplitPlan p = decode_plan(B, H, k);
   if (p.n_split <= 1) return 0;
   const size_t pairs = (size_t)B * p.n_split * H;
   return pairs * kDv * sizeof(uint16_t) + pairs * 2 * sizeof(float);
@@ -620,6 +1126,19 @@ size_t mla_decode_workspace_bytes(int B, int H, int Dv, int k) {
 hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t* idx, int R,
                            int H, int k, bool decode, float scale, uint16_t* out, float* lse,
                            void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!decode || decode_wide(R, H)) {
+    const float scale_log2 = scale * 1.44269504088896340736f;
+    SplitPlan p = decode ? split_plan_wide(R, H, k) : SplitPlan{1, k};
+    if (p.n_split > 1 && ws_bytes < mla_decode_workspace_bytes(R, H, kDv, k)) return hipErrorInvalidValue;
+    if (p.n_split <= 1) p = SplitPlan{1, k};
+    uint16_t* part_o = static_cast<uint16_t*>(ws);
+    float* part_ml = part_o ? reinterpret_cast<float*>(part_o + (size_t)R * p.n_split * H * kDv) : nullptr;
+    hipError_t e = wide_nw(H) == 4
+                       ? launch_wide<4>(q, kv, idx, R, H, k, decode, false, scale_log2, out, lse, part_o, part_ml, p, s)
+                       : launch_wide<2>(q, kv, idx, R, H, k, decode, false, scale_log2, out, lse, part_o, part_ml, p, s);
+    if (e != hipSuccess || p.n_split <= 1) return e;
+    return launch_combine(part_o, part_ml, R, H, p.n_split, out, lse, s);
+  }
   const float scale_log2 = scale * 1.44269504088896340736f;
   const uint16_t* kvp = static_cast<const uint16_t*>(kv.data);
   const int HG = H / kHeadsPerWg;
@@ -642,22 +1161,18 @@ hipError_t launch_mla_bf16(const uint16_t* q, const CacheView& kv, const int32_t
 #undef DSA_MLA_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split <= 1) return e;
-  const int RH = R * H;
-  const unsigned cgrid = (unsigned)((RH + kCombinePairs - 1) / kCombinePairs);
-  if (p.n_split <= 2)
-    mla_combine_kernel<2><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
-  else if (p.n_split <= 4)
-    mla_combine_kernel<4><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
-  else if (p.n_split <= 8)
-    mla_combine_kernel<8><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
-  else
-    mla_combine_kernel<16><<<cgrid, 256, 0, s>>>(part_o, part_ml, RH, H, p.n_split, out, lse);
-  return hipGetLastError();
+  return launch_combine(part_o, part_ml, R, H, p.n_split, out, lse, s);
 }
 
 hipError_t launch_mla_bf16_masked(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int T,
                                   int H, int k, float scale, uint16_t* out, float* lse, hipStream_t s) {
   const float scale_log2 = scale * 1.44269504088896340736f;
+  {
+    const CacheView v{kv, nullptr, nullptr, 0, 0, (int64_t)T};
+    return wide_nw(H) == 4
+               ? launch_wide<4>(q, v, idx, T, H, k, false, true, scale_log2, out, lse, nullptr, nullptr, SplitPlan{1, k}, s)
+               : launch_wide<2>(q, v, idx, T, H, k, false, true, scale_log2, out, lse, nullptr, nullptr, SplitPlan{1, k}, s);
+  }
   const unsigned grid = (unsigned)((int64_t)T * (H / kHeadsPerWg));
   const size_t lds = sizeof(uint32_t) * (size_t)((T + kTok - 1) / kTok);  // one live mask per tile
   mla_bf16_kernel<false, false, true><<<grid, kMlaThreads, lds, s>>>(

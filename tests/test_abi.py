@@ -78,11 +78,14 @@ def test_host_validation_paths():
     # generic kernel: logits of one (row, head) plus the query row in 64 KB of LDS
     assert L.dsa_sparse_mla_decode(dsa.F32, FAKE, ctypes.byref(kv), FAKE, 8, 128, 576, 512, 16000, 0.04, FAKE, None, None, 0, None) == 6
     # split plan, read back from the workspace size (B * splits * H partial rows of 512 bf16
-    # values + (max, sum)): ~256 workgroups at batch 8; no workgroup holds more than 8192
-    # kept tokens even when the batch alone fills the GPU
+    # values + (max, sum)): ~256 workgroups at batch 8 (64 heads each); from 64 sequences on
+    # the 128-head kernel, again ~256 workgroups; no workgroup holds more than 8192 kept tokens
     part = 512 * 2 + 8
     assert mw == 8 * 16 * 128 * part
-    assert L.dsa_sparse_mla_decode_workspace_size(128, 128, 512, 2048) == 0       # one split
+    assert L.dsa_sparse_mla_decode_workspace_size(32, 128, 512, 2048) == 32 * 4 * 128 * part
+    assert L.dsa_sparse_mla_decode_workspace_size(64, 128, 512, 2048) == 64 * 4 * 128 * part
+    assert L.dsa_sparse_mla_decode_workspace_size(128, 128, 512, 2048) == 128 * 2 * 128 * part
+    assert L.dsa_sparse_mla_decode_workspace_size(256, 128, 512, 2048) == 0       # one split
     assert L.dsa_sparse_mla_decode_workspace_size(128, 128, 512, 16384) == 128 * 2 * 128 * part
     assert L.dsa_sparse_mla_decode_workspace_size(512, 128, 512, 9000) == 512 * 2 * 128 * part
     # the no-allocation decode: same validation, plus the static array's size limit (checked on
