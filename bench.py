@@ -20,9 +20,12 @@ back-to-back indexer launches over the copies, with HIP events around its replay
 the indexer's launch duration for the roofline figure; an eager pass with events around
 each call gives the per-stage breakdown (host gaps included).
 
-`--mode prefill` times one causal prefill of T = 32768 tokens (workload 4) instead and reports
-the indexer (A2) against the FP8 MFMA peak and the sparse MLA (A6) against the bf16 MFMA peak,
-both as algorithmic flops over each kernel's own event-timed duration.
+`--mode prefill` times one causal prefill of T = 32768 tokens (workload 4) instead: the fused
+index + top-k (blocked, so no T x T score matrix exists) and the sparse MLA; the indexer and
+the top-k are also timed as the two separate calls over a full score matrix allocated for
+that diagnostic only.  It reports the indexer (A2) against the FP8 MFMA peak and the sparse
+MLA (A6) against the bf16 MFMA peak, both as algorithmic flops over each kernel's own
+event-timed duration.
 
 Prints one JSON line (rank 0, N = 1).  The library has no multi-GPU path.
 """
@@ -177,27 +180,33 @@ def main():
         spread = {"p10": float(np.percentile(per, 10)), "p50": float(np.median(per)),
                   "p90": float(np.percentile(per, 90)), "n": n_ev}
 
-    # ---- eager pass with HIP events around each op (on the stream the kernels run on)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # ---- eager pass with HIP events around each call: the step as run() issues it (the fused
+    # index + top-k, then attention), then the indexer and the top-k as two separate calls
+    # (over score rows the step itself never writes), for the per-stage breakdown
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for i in range(min(args.warmup, 5)):
         steps[i % len(steps)].run()
+        steps[i % len(steps)].index()
     torch.cuda.synchronize()
     te0 = time.perf_counter()
     for i in range(args.steps):
         st = steps[i % len(steps)]
         e = ev[i]
         e[0].record(stream)
-        st.index()
+        st.index_topk()
         e[1].record(stream)
-        st.topk()
-        e[2].record(stream)
         st.attend()
+        e[2].record(stream)
+        st.index()
         e[3].record(stream)
+        st.topk()
+        e[4].record(stream)
     torch.cuda.synchronize()
     te1 = time.perf_counter()
-    t_idx = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
-    t_topk = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
-    t_mla = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
+    t_fused = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    t_mla = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    t_idx = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
+    t_topk = np.array([e[3].elapsed_time(e[4]) for e in ev]) * 1e3
     idx_us = float(t_idx.mean())
     if use_graph:
         # the indexer's launch duration without host gaps: a graph of back-to-back indexer
@@ -238,7 +247,7 @@ def main():
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
         for a, b in evs:
             a.record(stream)
-            dsa.dsa_topk(buf, st0.ld, st0.n_valid, st0.B, st0.k, st0.idx, st0.topk_ws, st0.topk_ws_bytes, stream)
+            dsa.dsa_topk(buf, st0.ld, st0.n_valid, st0.B, st0.k, st0.idx, *st0.topk_ws, stream)
             b.record(stream)
         torch.cuda.synchronize()
         tie[name + "_us"] = float(np.mean([a.elapsed_time(b) for a, b in evs[2:]]) * 1e3)
@@ -405,8 +414,9 @@ def main():
                          "GB_s": append_bytes / (append_us * 1e3), "bound": "latency"},
         "topk_diagnostic": tie,
         "single_step_graph_us": single_us,
-        "breakdown_us": {"index": float(t_idx.mean()), "topk": float(t_topk.mean()), "sparse_mla": float(t_mla.mean()),
-                         "eager_step": (te1 - te0) * 1e6 / args.steps},
+        "breakdown_us": {"index_topk_fused": float(t_fused.mean()), "sparse_mla": float(t_mla.mean()),
+                         "index_alone": float(t_idx.mean()), "topk_alone": float(t_topk.mean()),
+                         "eager_step_and_separate_calls": (te1 - te0) * 1e6 / args.steps},
         "graph_replay_matches_eager": bool(ok),
         "cpu_baseline": cpu,
     }
@@ -440,19 +450,40 @@ def prefill(args):
     for _ in range(max(1, min(args.warmup, 2))):
         pf.run()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    # The step as run(): the fused index + top-k (blocked; no T x T score buffer), then attention.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in ev:
+        e[0].record(stream)
+        pf.index_topk()
+        e[1].record(stream)
+        pf.attend()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev])
+    t_fused, t_mla = (float(x) for x in ms.mean(axis=0))
+    total = t_fused + t_mla
+    fused_idx = pf.idx.clone()
+    # The indexer and the top-k as the two separate calls over the full [T, T] score matrix
+    # (allocated here for this diagnostic only), for the indexer's own kernel time.
+    pf.index()
+    pf.topk()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(fused_idx, pf.idx))
+    del fused_idx
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev2:
         e[0].record(stream)
         pf.index()
         e[1].record(stream)
         pf.topk()
         e[2].record(stream)
-        pf.attend()
-        e[3].record(stream)
     torch.cuda.synchronize()
-    ms = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in ev])
-    t_idx, t_topk, t_mla = (float(x) for x in ms.mean(axis=0))
-    total = t_idx + t_topk + t_mla
+    ms2 = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev2])
+    t_idx, t_topk = (float(x) for x in ms2.mean(axis=0))
+    score_matrix_bytes = pf.scores.numel() * 4
+    pf._scores = None
+    pf._topk_ws = None
+    torch.cuda.empty_cache()
     n = np.arange(1, T + 1, dtype=np.float64)
     idx_flops = float(n.sum()) * sh.HI * sh.dI * 2
     kept = np.minimum(n, sh.k)
@@ -493,7 +524,11 @@ def prefill(args):
         "data": "synthetic",
         "config": {"workload": cfg["name"], "tokens": T, "top_k": sh.k, "heads": sh.H, "latent": sh.Dqk,
                    "value_dim": sh.Dv, "indexer_heads": sh.HI, "indexer_dim": sh.dI},
-        "stages_ms": {"index": t_idx, "topk": t_topk, "sparse_mla": t_mla},
+        "stages_ms": {"index_topk_fused": t_fused, "sparse_mla": t_mla,
+                      "index_alone": t_idx, "topk_alone": t_topk},
+        "fused_same_as_two_calls": same,
+        "index_topk_workspace_bytes": pf.fused_ws_bytes,
+        "score_matrix_bytes_avoided": score_matrix_bytes,
         "short_prefill_t2048_attention": short,
         "roofline": {
             "index": {"bound": "mfma", "achieved": idx_tf, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -132,23 +132,46 @@ dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, c
 }
 
 namespace {
-struct FusedWs {
-  size_t scores, samp, topk, total;
+// The fused call on the fast indexer shape with few rows (decode) stores no score row: a
+// sample pass, the compacting indexer and the resolve (dsa::launch_index_topk_fused).  Other
+// calls (many rows: prefill; other shapes) score a block of rows into the workspace and
+// select from it, block after block, so the score buffer is bounded by kScoreBlockBytes
+// instead of growing with R x n_max.
+constexpr size_t kScoreBlockBytes = size_t(256) << 20;
+constexpr int kRowGroup = 7;  // rows per workgroup of the many-rows indexer: blocks keep its groups whole
+
+bool fused_fast(dsa_dtype dt, int H_I, int d_I) { return dt == DSA_E4M3 && H_I == 64 && d_I == 128; }
+bool fused_decode(int R, int64_t cap) { return R < dsa::index_rows_kernel_min() && dsa::index_topk_fused_ok(R, cap); }
+
+int block_rows(int R, int64_t cap) {
+  int64_t rb = (int64_t)(kScoreBlockBytes / (sizeof(float) * (size_t)cap)) / kRowGroup * kRowGroup;
+  rb = rb < kRowGroup ? kRowGroup : rb;
+  return (int)(rb < R ? rb : R);
+}
+
+struct BlockWs {
+  int rows;
+  size_t scores, topk, total;
 };
-FusedWs fused_ws(int R, int64_t cap, int k) {
+BlockWs block_ws(int R, int64_t cap, int k) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  FusedWs L{};
+  BlockWs L{};
+  L.rows = block_rows(R, cap);
   L.scores = 0;
-  L.samp = up(sizeof(float) * (size_t)R * (size_t)cap);
-  L.topk = L.samp + up(sizeof(float) * (size_t)R * 2048);
-  L.total = L.topk + up(dsa::topk_workspace_bytes(R, cap, k));
+  L.topk = up(sizeof(float) * (size_t)L.rows * (size_t)cap);
+  L.total = L.topk + up(dsa::topk_workspace_bytes(L.rows, cap, k));
   return L;
 }
 }  // namespace
 
 size_t dsa_index_topk_workspace_size(int R, int64_t n_max, int k) {
   if (R <= 0 || n_max <= 0 || k <= 0) return 0;
-  return fused_ws(R, n_max, k).total;
+  size_t need = block_ws(R, n_max, k).total;
+  if (fused_decode(R, n_max)) {
+    const size_t f = dsa::index_topk_fused_bytes(R, n_max);
+    need = f > need ? f : need;
+  }
+  return need;
 }
 
 dsa_status dsa_index_topk(dsa_dtype dt, const void* q, const float* q_scale, const float* w,
@@ -161,27 +184,37 @@ dsa_status dsa_index_topk(dsa_dtype dt, const void* q, const float* q_scale, con
   const int64_t cap = cache_capacity(keys);
   if (cap <= 0 || cap > (int64_t(1) << 24) || !dsa::topk_shape_ok(R, cap)) return DSA_ERR_SHAPE;
   if ((int64_t)H_I * d_I > 16384) return DSA_ERR_UNSUPPORTED;
-  const FusedWs L = fused_ws(R, cap, k);
-  if (!ws || ws_bytes < L.total) return DSA_ERR_WORKSPACE;
+  if (!ws) return DSA_ERR_WORKSPACE;
+  const dsa::CacheView kv = view(keys);
+  const bool fast = fused_fast(dt, H_I, d_I);
+  if (fast && fused_decode(R, cap)) {
+    if (ws_bytes < dsa::index_topk_fused_bytes(R, cap)) return DSA_ERR_WORKSPACE;
+    return launched(dsa::launch_index_topk_fused(static_cast<const uint8_t*>(q), q_scale, w, kv, row_seq,
+                                                 row_pos, R, cap, k, idx, ws, stream));
+  }
+  const BlockWs L = block_ws(R, cap, k);
+  if (ws_bytes < L.total) return DSA_ERR_WORKSPACE;
   char* b = static_cast<char*>(ws);
   float* scores = reinterpret_cast<float*>(b + L.scores);
-  float* samp = reinterpret_cast<float*>(b + L.samp);
   void* tws = b + L.topk;
-  const dsa::CacheView kv = view(keys);
-  hipError_t e;
-  if (dt == DSA_E4M3 && H_I == 64 && d_I == 128) {
-    // Decode-sized calls get the indexer's contiguous sample; calls with many rows (prefill)
-    // keep the many-rows indexer, and the top-k draws its sample from the score rows.
-    float* sp = R < dsa::index_rows_kernel_min() ? samp : nullptr;
-    e = dsa::launch_index_fp8_h64d128(static_cast<const uint8_t*>(q), q_scale, w, kv, row_seq, row_pos,
-                                      R, cap, scores, cap, stream, sp, dsa::topk_long_row_min(cap));
+  const size_t qrow = (size_t)H_I * d_I * (dt == DSA_E4M3 ? 1 : sizeof(float));
+  for (int r0 = 0; r0 < R; r0 += L.rows) {
+    const int nb = R - r0 < L.rows ? R - r0 : L.rows;
+    const void* qb = static_cast<const char*>(q) + (size_t)r0 * qrow;
+    const float* qsb = q_scale ? q_scale + r0 : nullptr;
+    const float* wb = w + (size_t)r0 * H_I;
+    hipError_t e;
+    if (fast)
+      e = dsa::launch_index_fp8_h64d128(static_cast<const uint8_t*>(qb), qsb, wb, kv, row_seq + r0, row_pos + r0,
+                                        nb, cap, scores, cap, stream);
+    else
+      e = dsa::launch_index_generic(dt == DSA_E4M3, qb, qsb, wb, kv, row_seq + r0, row_pos + r0, nb, H_I, d_I,
+                                    cap, scores, cap, stream);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
-    return launched(dsa::launch_topk(scores, cap, row_pos, R, k, idx, tws, stream, sp, 1));
+    e = dsa::launch_topk(scores, cap, row_pos + r0, nb, k, idx + (size_t)r0 * k, tws, stream, 1);
+    if (e != hipSuccess) return DSA_ERR_LAUNCH;
   }
-  e = dsa::launch_index_generic(dt == DSA_E4M3, q, q_scale, w, kv, row_seq, row_pos, R, H_I, d_I, cap,
-                                scores, cap, stream);
-  if (e != hipSuccess) return DSA_ERR_LAUNCH;
-  return launched(dsa::launch_topk(scores, cap, row_pos, R, k, idx, tws, stream, nullptr, 1));
+  return DSA_OK;
 }
 
 size_t dsa_indexer_quality_workspace_size(int R, int H, int64_t ld) {

@@ -9,67 +9,19 @@
 // Fast path (H_I = 64, d_I = 128, e4m3): one gfx950 v_mfma_scale_f32_16x16x128_f8f6f4
 // per 16 heads x 16 keys covers the whole 128-byte key row, so a key is read from HBM
 // exactly once and multiplied against all 64 query heads held in registers.  The
-// ReLU / w-weighted head sum / per-token scale run in fp32 on the MFMA results.
+// ReLU / w-weighted head sum / per-token scale run in fp32 on the MFMA results
+// (score_core.h).
 #include "common.h"
 #include "kernels.h"
+#include "score_core.h"
+#include "select_core.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kIdxWaves = 8;
 typedef int v4i __attribute__((ext_vector_type(4)));
-constexpr int kIdxBatch = 64;  // keys per wave per loop trip: four 16-key MFMA column groups
-
-// Scores of one trip of 64 keys for 64 heads.  kb[u] holds lane (col, grp)'s 32 key bytes of
-// key 16*u + col (k-slice grp), qa[ht] the matching query bytes of heads 16*ht + col, wr the
-// weights of the heads the result layout leaves in this lane (16*ht + 4*grp + i).  Returns,
-// in lane l, the weighted ReLU head sum of key l of the trip (before the scales).
-__device__ __forceinline__ float trip_scores(const v8i (&qa)[4], const float (&wr)[4][4], const v8i (&kb)[4]) {
-  float part[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    // The four head groups' products go out back to back into separate accumulators, so the
-    // ReLU-weight epilogue of one overlaps the MFMAs still in flight instead of waiting on each.
-    v4f acc[4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      // cbsz/blgp = 0: both operands OCP e4m3; scale exponent 127 = x1.
-      acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb[u], v4f{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                 0, 0, 0, 127, 0, 127);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the four MFMAs ahead of the epilogue
-    float sum = 0.0f;
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sum = fmaf(wr[ht][i], __builtin_amdgcn_fmed3f(acc[ht][i], 0.0f, 3.0e38f), sum);
-    part[u] = sum;
-  }
-  // Stage 1 (lanes l, l^32): lower half keeps groups 0/1, upper half 2/3.
-  const v2i x02 = __builtin_amdgcn_permlane32_swap(__float_as_int(part[0]), __float_as_int(part[2]), false, false);
-  const v2i x13 = __builtin_amdgcn_permlane32_swap(__float_as_int(part[1]), __float_as_int(part[3]), false, false);
-  const float h02 = __int_as_float(x02[0]) + __int_as_float(x02[1]);
-  const float h13 = __int_as_float(x13[0]) + __int_as_float(x13[1]);
-  // Stage 2 (rows of 16 lanes, r and r^1): row g ends with group g's full sum.
-  const v2i y = __builtin_amdgcn_permlane16_swap(__float_as_int(h02), __float_as_int(h13), false, false);
-  return __int_as_float(y[0]) + __int_as_float(y[1]);
-}
-
-// Query fragments and head weights of one row in the lane layout trip_scores expects.
-__device__ __forceinline__ void load_query(const uint8_t* __restrict__ qr, const float* __restrict__ wrow,
-                                           int col, int grp, v8i (&qa)[4], float (&wr)[4][4]) {
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const uint4* p = reinterpret_cast<const uint4*>(qr + (16 * ht + col) * 128 + 32 * grp);
-    const uint4 a = p[0], b = p[1];
-    qa[ht] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-  }
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const float4 v = *reinterpret_cast<const float4*>(wrow + 16 * ht + 4 * grp);
-    wr[ht][0] = v.x; wr[ht][1] = v.y; wr[ht][2] = v.z; wr[ht][3] = v.w;
-  }
-}
+constexpr int kCompactTrips = 8;  // most trips per wave of the compacting indexer (4096 keys per workgroup)
 
 // Score of 64 keys per loop trip and wave.  Lane (col, grp) feeds key s0 + 16*u + col, bytes
 // 32*grp .. 32*grp+31, to the MFMA of column group u; the result layout leaves the lane with
@@ -78,27 +30,97 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ qr, const
 // partial sums of each group and leaves group g's totals in lanes 16*g .. 16*g+15, so the 64
 // scores of the trip leave in one coalesced 256-byte store.
 //
-// SAMPLE (the fused index + top-k call): rows longer than samp_min_n also store the scores
-// at the evenly spaced positions (i * n) / kIdxSample, i < kIdxSample, contiguously in
-// samp[r, i], where the top-k's threshold search reads them as one 8 KB block instead of
-// 2048 scattered scores of the row.
-constexpr int kIdxSample = 2048;
-template <bool PAGED, bool SAMPLE = false>
+// COMPACT (the fused index + top-k call): no score is stored.  The grid has R extra blocks
+// in front: block r scores row r's kCompactSample evenly spaced keys (positions
+// (i * n) / kCompactSample) and publishes the row's threshold theta -- about 3k survivors
+// expected -- in hdr[r] and in the word ready[r].  Every other block scores its chunk, parks
+// the keys in LDS and only then reads ready[r] (by then the sample block, dispatched first
+// and far less work, has long published it); it writes only the survivors (key >= theta) as
+// (key, position) pairs, in position order, to the chunk's slot of the candidate buffer, with
+// the chunk's counts of keys above theta and equal to it and the theta it used.  The wait is
+// bounded: a chunk that finds no threshold keeps nothing and records so, and the resolve
+// rescores such a row.  Rows of at most min_n keys are skipped (their selection needs no
+// scores).
+constexpr int kCompactSample = 1024;  // 8 waves x 2 trips
+constexpr int kThetaPolls = 2048;     // ~2 ms of polling (s_sleep 32 between reads)
+constexpr int kSampleWords = kCompactSample + kPassMax * kHistBins + (int)(sizeof(SelState) + 3) / 4;
+constexpr int kParkWords = kIdxWaves * kCompactTrips * kIdxBatch;
+constexpr int kPoolWords = kSampleWords > kParkWords ? kSampleWords : kParkWords;
+
+// The sample block of row r (all threads of the block).
+__device__ void compact_sample_block(int r, const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+                                     const float* __restrict__ w, const uint8_t* __restrict__ kdata,
+                                     const float* __restrict__ kscale, const KeyRows& kr,
+                                     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
+                                     int min_n, RowHeader* __restrict__ hdr, uint64_t* __restrict__ ready,
+                                     uint8_t* sq, float* sw, uint32_t* pool) {
+  const int64_t n = (int64_t)row_pos[r] + 1;
+  if (n <= min_n) return;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int col = lane & 15, grp = lane >> 4;
+  const int seq = row_seq[r];
+  for (int i = tid; i < 64 * 128 / 16; i += kIdxWaves * WAVE)
+    reinterpret_cast<uint4*>(sq)[i] = reinterpret_cast<const uint4*>(q + (int64_t)r * (64 * 128))[i];
+  if (tid < 64) sw[tid] = w[(int64_t)r * 64 + tid];
+  __syncthreads();
+  v8i qa[4];
+  float wr[4][4];
+  load_query(sq, sw, col, grp, qa, wr);
+  const float qs = q_scale ? q_scale[r] : 1.0f;
+  uint32_t* samp = pool;
+  int* hist = reinterpret_cast<int*>(pool + kCompactSample);
+  SelState& st = *reinterpret_cast<SelState*>(pool + kCompactSample + kPassMax * kHistBins);
+  uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j0 = (2 * wave + t) * kIdxBatch;
+    v8i kb[4];
+    load_trip(kdata, kr, seq, col, grp, [&](int j) { return (int64_t)(j0 + j) * n / kCompactSample; }, kb);
+    const float ks = kscale ? kscale[kr.row(seq, (int64_t)(j0 + lane) * n / kCompactSample)] : 1.0f;
+    const uint32_t key = float_key(scaled_score(trip_scores(qa, wr, kb), ks, qs));
+    samp[j0 + lane] = key;
+    lmn = min(lmn, key);
+    lmx = max(lmx, key);
+  }
+  const RowHeader rh = sample_header<kIdxWaves * WAVE>(samp, kCompactSample, 3, lmn, lmx, n, min_n, hist, st);
+  if (tid == 0) {
+    hdr[r] = rh;
+    __hip_atomic_store(&ready[r], ((uint64_t)kThetaReady << 32) | rh.theta, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <bool PAGED, bool COMPACT = false>
 __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kdata, const float* __restrict__ kscale,
     const int32_t* __restrict__ table, int max_pages, int page_size, int page_shift,
     int64_t seq_stride, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
     float* __restrict__ scores, int64_t ld, int keys_per_wg, int n_chunks,
-    float* __restrict__ samp = nullptr, int samp_min_n = 0) {
+    RowHeader* __restrict__ hdr = nullptr, uint64_t* __restrict__ ready = nullptr,
+    ChunkCount* __restrict__ counts = nullptr, uint2* __restrict__ cand = nullptr, int min_n = 0,
+    int n_rows = 0) {
+  // The row's query (8 KB) and head weights go to LDS once; every wave reads its fragments
+  // there instead of fetching its own copy through L2.
+  __shared__ __attribute__((aligned(16))) uint8_t sq[64 * 128];
+  __shared__ __attribute__((aligned(16))) float sw[64];
+  __shared__ __attribute__((aligned(16))) uint32_t pool[COMPACT ? kPoolWords : 1];
+  if (COMPACT && (int)blockIdx.x < n_rows) {
+    compact_sample_block(blockIdx.x, q, q_scale, w, kdata, kscale,
+                         KeyRows{PAGED ? table : nullptr, max_pages, page_size, page_shift, seq_stride}, row_seq,
+                         row_pos, min_n, hdr, ready, sq, sw, pool);
+    return;
+  }
+  const int blk = COMPACT ? (int)blockIdx.x - n_rows : (int)blockIdx.x;
   extern __shared__ int spage[];  // paged: physical page of each logical page of this range
   // Block b takes chunk b % n_chunks of row b / n_chunks: consecutive blocks (which the
   // dispatcher deals round-robin to the eight XCDs) walk along a row, so rows of different
   // lengths still spread their work evenly over the XCDs.
-  const int r = blockIdx.x / n_chunks;
+  const int r = blk / n_chunks;
+  const int chunk = blk % n_chunks;
   const int64_t n = (int64_t)row_pos[r] + 1;
-  const int64_t wg_begin = (int64_t)(blockIdx.x % n_chunks) * keys_per_wg;
-  if (wg_begin >= n) return;
+  const int64_t wg_begin = (int64_t)chunk * keys_per_wg;
+  if (wg_begin >= n || (COMPACT && n <= min_n)) return;
   const int64_t wg_end = min(wg_begin + keys_per_wg, n);
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
@@ -118,10 +140,6 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
 
   // A operand: q[r, 16*ht + col, 32*grp .. 32*grp+31] (e4m3 bytes); result rows held by
   // this lane are heads 16*ht + 4*grp + i.
-  // The row's query (8 KB) and head weights go to LDS once; every wave reads its fragments
-  // there instead of fetching its own copy through L2.
-  __shared__ __attribute__((aligned(16))) uint8_t sq[64 * 128];
-  __shared__ __attribute__((aligned(16))) float sw[64];
   for (int i = tid; i < 64 * 128 / 16; i += kIdxWaves * WAVE)
     reinterpret_cast<uint4*>(sq)[i] = reinterpret_cast<const uint4*>(q + (int64_t)r * (64 * 128))[i];
   if (tid < 64) sw[tid] = w[(int64_t)r * 64 + tid];
@@ -133,7 +151,6 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
   const int per_wave = keys_per_wg / kIdxWaves;
   const int64_t wbeg = wg_begin + (int64_t)wave * per_wave;
   const int64_t wend = min(wbeg + per_wave, n);
-  float* srow = scores + (int64_t)r * ld;
 
   auto row_of = [&](int64_t s) -> int64_t {
     if (PAGED) {
@@ -144,7 +161,8 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     return (int64_t)seq * seq_stride + s;
   };
 
-  for (int64_t s0 = wbeg; s0 < wend; s0 += kIdxBatch) {
+  // The score of key s0 + lane (s0 < wend; lanes past wend return the last key's score).
+  auto trip = [&](int64_t s0) -> float {
     // Addresses are clamped to the last valid key instead of branching, so every load issues.
     // Keys are read once per call.  Contiguous caches stream them with non-temporal loads
     // (faster here, and the later kernels of the step run faster too); paged caches, whose
@@ -165,23 +183,71 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
       }
       kb[u] = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
-    const int64_t s_out = s0 + lane;  // the key whose score this lane writes
-    const float ks = kscale ? kscale[row_of(min(s_out, wend - 1))] : 1.0f;
-    const float tot = trip_scores(qa, wr, kb);
-    const float score = tot * ks * qs;
-    if (s_out < wend) srow[s_out] = score;
-    if (SAMPLE && n > samp_min_n && s_out < wend) {
-      // s_out is sample i's position when (i * n) / kIdxSample == s_out, i.e. for
-      // i = ceil(s_out * kIdxSample / n); a float estimate of s_out * kIdxSample / n (error far
-      // below 1) leaves that i at its floor or one above, both checked exactly.
-      const int64_t ie = (int64_t)((float)s_out * ((float)kIdxSample / (float)n));
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const int64_t i = ie + d;
-        if (i < kIdxSample && (i * n) / kIdxSample == s_out) samp[(int64_t)r * kIdxSample + i] = score;
-      }
+    const float ks = kscale ? kscale[row_of(min(s0 + lane, wend - 1))] : 1.0f;
+    return scaled_score(trip_scores(qa, wr, kb), ks, qs);
+  };
+
+  if (!COMPACT) {
+    float* srow = scores + (int64_t)r * ld;
+    for (int64_t s0 = wbeg; s0 < wend; s0 += kIdxBatch) {
+      const float score = trip(s0);
+      if (s0 + lane < wend) srow[s0 + lane] = score;
     }
+    return;
   }
+
+  // ---- compaction.  The trips' keys are parked in LDS (registers are what limits this kernel
+  // to two workgroups per CU); 0 stands for "no key" and is below every real score's key.
+  uint32_t* s_key = pool;  // [wave][trip][lane]
+  int nt = 0;
+  for (int64_t s0 = wbeg; s0 < wend; s0 += kIdxBatch, ++nt) {
+    const float score = trip(s0);
+    s_key[(wave * kCompactTrips + nt) * kIdxBatch + lane] = s0 + lane < wend ? float_key(score) : 0u;
+  }
+  __shared__ uint32_t s_theta;
+  if (tid == 0) {
+    uint64_t v = 0;
+    bool ok = false;
+    for (int it = 0; it < kThetaPolls && !ok; ++it) {
+      v = __hip_atomic_load(&ready[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = (uint32_t)(v >> 32) == kThetaReady;
+      if (!ok) __builtin_amdgcn_s_sleep(32);
+    }
+    // No threshold: keep nothing; the recorded theta cannot match the row's, so the resolve
+    // rescores the row.
+    s_theta = ok ? (uint32_t)v : 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  const uint32_t theta = s_theta;
+  __shared__ int s_cnt[2][kIdxWaves];
+  int gt = 0, eq = 0;
+  for (int t = 0; t < nt; ++t) {
+    const uint32_t key = s_key[(wave * kCompactTrips + t) * kIdxBatch + lane];
+    gt += __popcll(ballot(key > theta));
+    eq += __popcll(ballot(key == theta));
+  }
+  if (lane == 0) {
+    s_cnt[0][wave] = gt;
+    s_cnt[1][wave] = eq;
+  }
+  __syncthreads();
+  int off = 0, G = 0, E = 0;
+#pragma unroll
+  for (int v = 0; v < kIdxWaves; ++v) {
+    const int a = s_cnt[0][v], b = s_cnt[1][v];
+    off += v < wave ? a + b : 0;
+    G += a;
+    E += b;
+  }
+  uint2* cr = cand + (int64_t)r * ld + wg_begin;
+  for (int t = 0; t < nt; ++t) {
+    const uint32_t key = s_key[(wave * kCompactTrips + t) * kIdxBatch + lane];
+    const bool keep = key >= theta;
+    const uint64_t km = ballot(keep);
+    if (keep) cr[off + mask_rank(km)] = make_uint2(key, (uint32_t)(wbeg + (int64_t)t * kIdxBatch + lane));
+    off += __popcll(km);
+  }
+  if (tid == 0) counts[(int64_t)r * n_chunks + chunk] = ChunkCount{(uint32_t)G, (uint32_t)E, theta, 0u};
 }
 
 // Many rows (prefill): one workgroup scores kRowsPerWg consecutive rows against one key range.
@@ -282,7 +348,7 @@ __global__ __launch_bounds__(kRowsThreads) void index_fp8_rows_kernel(
       const int64_t s_out = s0 + lane;
       const float ks = kscale ? kscale[row_in(seq, min(s_out, end - 1), nullptr, 0)] : 1.0f;
       const float tot = trip_scores(qa, wr, kb);
-      if (s_out < end) srow[s_out] = tot * ks * qs;
+      if (s_out < end) srow[s_out] = scaled_score(tot, ks, qs);
     }
     return;
   }
@@ -359,7 +425,7 @@ __global__ __launch_bounds__(kRowsThreads) void index_fp8_rows_kernel(
     const float ks = kscale ? *reinterpret_cast<const float*>(tb + 8192 + 4 * lane) : 1.0f;
     const float tot = trip_scores(qa, wr, kb);
     const int64_t s_out = c0 + (int64_t)t * kIdxBatch + lane;
-    if (s_out < end) srow[s_out] = tot * ks * qs;
+    if (s_out < end) srow[s_out] = scaled_score(tot, ks, qs);
   };
   for (int t = 0; t < ntrips; t += kKeyRing) {
     step(KeySlot<0>{}, t);
@@ -414,12 +480,21 @@ __global__ __launch_bounds__(256) void index_generic_kernel(
 
 int index_rows_kernel_min() { return kRowsKernelMin; }
 
+// Keys per workgroup of the one-row-per-workgroup indexer: ~512 workgroups of 8 waves (two
+// per CU at its register use); each wave's share is a multiple of the 64-key trip.
+int index_keys_per_wg(int R, int64_t n_bound) {
+  const int64_t total = (int64_t)R * n_bound;
+  int64_t kpw = 512;
+  while (kpw < 64 * kIdxWaves * kCompactTrips && total / (kpw * 2) >= 512) kpw *= 2;
+  return (int)kpw;
+}
+
 hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, const float* w,
                                     const CacheView& keys, const int32_t* row_seq,
                                     const int32_t* row_pos, int R, int64_t n_bound, float* scores,
-                                    int64_t ld, hipStream_t s, float* samp, int samp_min_n) {
+                                    int64_t ld, hipStream_t s) {
   const uint8_t* kd = static_cast<const uint8_t*>(keys.data);
-  if (R >= kRowsKernelMin && !samp) {
+  if (R >= kRowsKernelMin) {
     // Many rows: seven rows per workgroup sharing staged key trips; 4096 keys per workgroup.
     const int64_t kpw = 4096;
     const dim3 grid((unsigned)((R + kRowsPerWg - 1) / kRowsPerWg), (unsigned)((n_bound + kpw - 1) / kpw));
@@ -437,34 +512,44 @@ hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, cons
     }
     return hipGetLastError();
   }
-  // ~512 workgroups of 8 waves (two per CU at this kernel's register use); each wave's
-  // share is a multiple of the 64-key trip.
-  const int64_t total = (int64_t)R * n_bound;
-  int64_t kpw = 512;
-  while (kpw < 4096 && total / (kpw * 2) >= 512) kpw *= 2;
+  const int kpw = index_keys_per_wg(R, n_bound);
   const int n_chunks = (int)((n_bound + kpw - 1) / kpw);
   const unsigned grid = (unsigned)R * (unsigned)n_chunks;
   if (keys.table) {
     const int ps = keys.page_size;
     const int shift = (ps & (ps - 1)) == 0 ? __builtin_ctz(ps) : -1;
     const size_t lds = sizeof(int) * (size_t)(kpw / ps + 2);
-    if (samp)
-      index_fp8_kernel<true, true><<<grid, kIdxWaves * WAVE, lds, s>>>(
-          q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
-          scores, ld, (int)kpw, n_chunks, samp, samp_min_n);
-    else
-      index_fp8_kernel<true><<<grid, kIdxWaves * WAVE, lds, s>>>(
-          q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
-          scores, ld, (int)kpw, n_chunks);
+    index_fp8_kernel<true><<<grid, kIdxWaves * WAVE, lds, s>>>(
+        q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
+        scores, ld, kpw, n_chunks);
   } else {
-    if (samp)
-      index_fp8_kernel<false, true><<<grid, kIdxWaves * WAVE, 0, s>>>(
-          q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, scores,
-          ld, (int)kpw, n_chunks, samp, samp_min_n);
-    else
-      index_fp8_kernel<false><<<grid, kIdxWaves * WAVE, 0, s>>>(
-          q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, scores,
-          ld, (int)kpw, n_chunks);
+    index_fp8_kernel<false><<<grid, kIdxWaves * WAVE, 0, s>>>(
+        q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, scores,
+        ld, kpw, n_chunks);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index_fp8_compact(const uint8_t* q, const float* q_scale, const float* w,
+                                    const CacheView& keys, const int32_t* row_seq,
+                                    const int32_t* row_pos, int R, int64_t n_bound, int64_t ld,
+                                    RowHeader* hdr, uint64_t* ready, ChunkCount* counts, uint2* cand,
+                                    int min_n, hipStream_t s) {
+  const uint8_t* kd = static_cast<const uint8_t*>(keys.data);
+  const int kpw = index_keys_per_wg(R, n_bound);
+  const int n_chunks = (int)((n_bound + kpw - 1) / kpw);
+  const unsigned grid = (unsigned)R + (unsigned)R * (unsigned)n_chunks;  // sample blocks first
+  if (keys.table) {
+    const int ps = keys.page_size;
+    const int shift = (ps & (ps - 1)) == 0 ? __builtin_ctz(ps) : -1;
+    const size_t lds = sizeof(int) * (size_t)(kpw / ps + 2);
+    index_fp8_kernel<true, true><<<grid, kIdxWaves * WAVE, lds, s>>>(
+        q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
+        nullptr, ld, kpw, n_chunks, hdr, ready, counts, cand, min_n, R);
+  } else {
+    index_fp8_kernel<false, true><<<grid, kIdxWaves * WAVE, 0, s>>>(
+        q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, nullptr,
+        ld, kpw, n_chunks, hdr, ready, counts, cand, min_n, R);
   }
   return hipGetLastError();
 }

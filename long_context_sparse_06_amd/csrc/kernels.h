@@ -15,17 +15,41 @@ struct CacheView {
   int64_t seq_stride;
 };
 
+// Hand-off of the sampled long-row top-k between its passes (and from the compacting indexer).
+struct RowHeader {
+  uint32_t theta;  // sample threshold key of a long row
+  uint32_t shift;  // survivor bin of key = min((key - theta) >> shift, 4095)
+};
+struct ChunkCount {
+  uint32_t gt;     // survivors of a chunk above theta
+  uint32_t eq;     // survivors of a chunk equal to theta
+  uint32_t theta;  // the threshold the chunk was compacted with
+  uint32_t pad;
+};
+// A row threshold published inside the compacting indexer: (kThetaReady << 32) | theta.
+constexpr uint32_t kThetaReady = 0x7E7A5EEDu;
+
 // ---- indexer
-// samp (optional): rows longer than samp_min_n also store their 2048 evenly spaced sample
-// scores contiguously in samp[R, 2048] (positions (i * n) / 2048); the rows kernel for many
-// rows is not used then.
-// Calls with at least this many rows (and no sample wanted) use the many-rows kernel.
+// Calls with at least this many rows use the many-rows kernel.
 int index_rows_kernel_min();
+// Keys per workgroup (the compaction chunk) of the one-row-per-workgroup indexer for R rows
+// of at most n_bound keys.
+int index_keys_per_wg(int R, int64_t n_bound);
 hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, const float* w,
                                     const CacheView& keys, const int32_t* row_seq,
                                     const int32_t* row_pos, int R, int64_t n_bound, float* scores,
-                                    int64_t ld, hipStream_t s, float* samp = nullptr,
-                                    int samp_min_n = 0);
+                                    int64_t ld, hipStream_t s);
+// Scores rows longer than min_n without storing them.  R extra workgroups score each row's
+// sample and publish its threshold (hdr[r], and the word ready[r] the scoring workgroups poll);
+// the survivors of that threshold go to the chunk slots of cand [R, ld] with per-chunk counts
+// [R, ceil(n_bound / chunk)].  ready[r] must not hold a published word of an earlier call
+// (the resolve clears it); if it does, chunks may be compacted with a stale threshold, which
+// the resolve detects (ChunkCount::theta) and answers by rescoring the row.
+hipError_t launch_index_fp8_compact(const uint8_t* q, const float* q_scale, const float* w,
+                                    const CacheView& keys, const int32_t* row_seq,
+                                    const int32_t* row_pos, int R, int64_t n_bound, int64_t ld,
+                                    RowHeader* hdr, uint64_t* ready, ChunkCount* counts, uint2* cand,
+                                    int min_n, hipStream_t s);
 hipError_t launch_index_generic(bool fp8, const void* q, const float* q_scale, const float* w,
                                 const CacheView& keys, const int32_t* row_seq, const int32_t* row_pos,
                                 int R, int HI, int dI, int64_t n_bound, float* scores, int64_t ld,
@@ -35,14 +59,19 @@ hipError_t launch_index_generic(bool fp8, const void* q, const float* q_scale, c
 size_t topk_workspace_bytes(int R, int64_t ld, int k);
 // False when R rows of length ld need more blocks than one launch can take.
 bool topk_shape_ok(int R, int64_t ld);
-// samp (optional): each long row's 2048 sample scores, contiguous (see the indexer);
-// the rows' lengths are n_valid[r] + n_off.
+// Row r has n_valid[r] + n_off scores.
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
-                       int32_t* idx, void* ws, hipStream_t s, const float* samp = nullptr,
-                       int n_off = 0);
-// Rows longer than this use the sampled compaction (and so want the indexer's sample), for
-// score rows of leading dimension ld.
+                       int32_t* idx, void* ws, hipStream_t s, int n_off = 0);
+// Rows longer than this use the sampled compaction, for score rows of leading dimension ld.
 int topk_long_row_min(int64_t ld);
+
+// ---- fused index + top-k, fast indexer shape (64 heads x 128, e4m3): sample pass, compacting
+// indexer, resolve -- no score row is stored.  Rows are row_pos[r] + 1 keys long, ld >= each.
+size_t index_topk_fused_bytes(int R, int64_t ld);
+bool index_topk_fused_ok(int R, int64_t ld);
+hipError_t launch_index_topk_fused(const uint8_t* q, const float* q_scale, const float* w, const CacheView& keys,
+                                   const int32_t* row_seq, const int32_t* row_pos, int R, int64_t ld, int k,
+                                   int32_t* idx, void* ws, hipStream_t s);
 
 // ---- sparse MLA
 size_t mla_decode_workspace_bytes(int B, int H, int Dv, int k);

@@ -6,390 +6,65 @@
 // in MarkTechPost's "Training signal" paragraph).  The tie rule and the output order
 // (ascending index, -1 padded) are this library's.
 //
-// Method: radix select on order-preserving 32-bit keys held in LDS.  A min/max pass
-// first strips the bits all keys share, so the 11-bit histogram digits land where the
-// keys actually differ; each digit pass narrows to one bin until either that bin holds
-// exactly the elements still needed or the full key (the threshold T) is known.  Every
-// search step is block-parallel (DPP wave scans, per-wave totals through LDS); no phase
-// runs on a single wave.  The emit pass walks each wave's contiguous index range with
-// ballots, so the elements equal to T are taken lowest index first and the output comes
-// out sorted.
+// Method: the radix select and ordered emit of select_core.h.
 //
 // Rows up to kRowMax scores (up to kLongMinWs when the call's rows are longer than kRowMax, so
 // the compaction workspace exists) are selected by one workgroup that holds the row in
 // registers (read from memory once) and keeps only the histograms in LDS.  Longer rows
-// (decode at 128k context) take three launches: one workgroup per row draws an evenly
-// spaced sample and sets a threshold theta whose expected survivor count is ~2k; many
-// workgroups per row compact the survivors (in index order); one workgroup per row then
-// gathers them into LDS, histogramming them into 4096 bins above theta on the way, so the
-// bin holding the k-th largest survivor is known after one block scan, and ranks the few
-// keys of that bin by direct comparison.  The hand-offs are kernel boundaries: an in-kernel
-// device-scope fence costs a whole-L2 writeback and invalidate on this chip.
-// Correctness never depends on the sample: if fewer than k or more than fit in LDS
-// survive, the resolve selects from the full row in global memory instead, and a
-// crowded boundary bin falls back to the radix select over the survivors.
+// (decode at 128k context) take a sampled compaction: a threshold theta whose expected
+// survivor count is ~2k comes from an evenly spaced sample of 2048 scores; many workgroups
+// per row compact the survivors (in index order, counting those above theta and those equal
+// to it per chunk); one workgroup per row then resolves them.  The hand-offs are kernel
+// boundaries: an in-kernel device-scope fence costs a whole-L2 writeback and invalidate on
+// this chip.  The resolve has three cases:
+//   * theta is the threshold itself (fewer than k keys above it, at least k at or above it,
+//     as on a row of equal scores): every key above theta and the first keys equal to it
+//     are taken, copied straight from the chunks' candidate slots;
+//   * up to 12288 survivors: they are gathered into LDS, histogrammed into 4096 bins above
+//     theta on the way, so the bin holding the k-th largest is known after one block scan,
+//     and the few keys of that bin are ranked by direct comparison;
+//   * otherwise (fewer than k survivors, or too many with at least k above theta): the
+//     radix select over the whole row in global memory.
+// Correctness never depends on the sample, only the speed does.
+//
+// The fused index + top-k call runs the same resolve without any score row: the compacting
+// indexer (indexer.hip, COMPACT) scores each row's sample in workgroups of its own and
+// compacts the survivors as it scores; the resolve checks that every chunk used the row's
+// threshold, and its last case rescores the row into the candidate buffer first.
 #include "common.h"
 #include "kernels.h"
+#include "score_core.h"
+#include "select_core.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kRowMax = 32768;     // longest row selected by one workgroup (32 keys per thread)
-constexpr int kSample = 2048;      // sample size for longer rows
+constexpr int kSample = 2048;      // sample size for longer rows (from stored score rows)
 constexpr int kChunk = 4096;       // scores per workgroup in the long-row compaction pass
 // When the call has a candidate workspace (ld > kRowMax), rows longer than this already take
 // the sampled compaction: a single workgroup's multi-pass radix select over 8k..32k scores
 // is slower than the compaction and resolve.
 constexpr int kLongMinWs = 8192;
 constexpr int kCandCap = 12288;    // survivors resolvable in LDS (96 KiB of key/index pairs)
-constexpr int kHistBins = 2048;    // 11-bit digits
-constexpr int kPassMax = 3;        // range-relative 11-bit digits resolve 32-bit keys in 3 passes
-constexpr int kSurvBins = 4096;    // survivor histogram of a long row
 constexpr int kTieMax = 256;       // largest boundary bin ranked by pairwise comparison
+constexpr int kFusedMaxChunks = 4096;  // chunk offsets of a fused call's row that fit the resolve's LDS
 constexpr int kRowThreads = 1024;
 constexpr int kLongThreads = 256;  // compaction workgroups
 constexpr int kResolveThreads = 1024;
 
-struct RowHeader {
-  uint32_t theta;  // sample threshold key of a long row
-  uint32_t shift;  // survivor bin of key = min((key - theta) >> shift, kSurvBins - 1)
-};
-
-// Block-shared scratch of the selection routines.
-struct SelState {
-  uint32_t wmin[16], wmax[16];      // per-wave key range
-  uint32_t wred[16];                // per-wave partials of a caller's final reduction
-  alignas(16) int wscan[16];        // per-wave bin totals of a crossing search
-  alignas(16) int wtot[2][16];      // per-wave counts of the emit pass
-  int digit, above, cnt;            // result of a crossing search
-  uint32_t tie_T;                   // result of the boundary-bin ranking
-  int tie_need;
-  int ntie;
-};
-
-// ---- element sources --------------------------------------------------------------
-struct LdsKeys {  // keys in LDS, ids = position + base
-  const uint32_t* keys;
-  int base;
-  __device__ uint32_t key(int i) const { return keys[i]; }
-  __device__ int id(int i) const { return base + i; }
-};
-struct LdsPairs {  // keys and ids in LDS
-  const uint32_t* keys;
-  const int* ids;
-  __device__ uint32_t key(int i) const { return keys[i]; }
-  __device__ int id(int i) const { return ids[i]; }
-};
-struct GlobalRow {  // a score row in global memory
-  const float* row;
-  __device__ uint32_t key(int i) const { return float_key(row[i]); }
-  __device__ int id(int i) const { return i; }
-};
-
-// Visits elements i = tid, tid + NT, ... of [0, m) in batches of U per thread: all U keys of a
-// batch are read before any is used, so global-memory sources have U loads in flight
-// instead of one round trip per element.
-template <int NT, int U, class Src, class F>
-__device__ __forceinline__ void for_each_key(const Src& src, int m, F&& f) {
-  for (int base = 0; base < m; base += NT * U) {
-    uint32_t kv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * NT + (int)threadIdx.x;
-      kv[u] = src.key(min(i, m - 1));  // unconditional: the batch's loads issue back to back
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * NT + (int)threadIdx.x;
-      if (i < m) f(i, kv[u]);
-    }
-  }
-}
-
-// ---- wave primitives: DPP row shifts/rotations and gfx950 lane swaps (no LDS traffic) ----
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ int dpp(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
-}
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  v += dpp<0x111>(v);        // row_shr:1
-  v += dpp<0x112>(v);        // row_shr:2
-  v += dpp<0x114>(v);        // row_shr:4
-  v += dpp<0x118>(v);        // row_shr:8  -> inclusive within rows of 16
-  v += dpp<0x142, 0xA>(v);   // row_bcast:15 -> rows 1 and 3 add the previous row's total
-  v += dpp<0x143, 0xC>(v);   // row_bcast:31 -> rows 2 and 3 add rows 0-1
-  return v;
-}
-// All-lane reductions: rotations within rows of 16, then swaps across rows and halves.
-template <class F>
-__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, F op) {
-  v = op(v, (uint32_t)dpp<0x128>((int)v));  // row_ror:8
-  v = op(v, (uint32_t)dpp<0x124>((int)v));  // row_ror:4
-  v = op(v, (uint32_t)dpp<0x122>((int)v));  // row_ror:2
-  v = op(v, (uint32_t)dpp<0x121>((int)v));  // row_ror:1
-  const v2i a = __builtin_amdgcn_permlane16_swap((int)v, (int)v, false, false);
-  v = op((uint32_t)a[0], (uint32_t)a[1]);
-  const v2i b = __builtin_amdgcn_permlane32_swap((int)v, (int)v, false, false);
-  return op((uint32_t)b[0], (uint32_t)b[1]);
-}
-struct UMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
-struct UMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
-
-__device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
-
-// The top-k threshold: the selection is { key > T } plus the `need` lowest-index elements
-// equal to T, or exactly { key >= T } when `exact`.  `top` is the largest key seen.
-struct Threshold {
-  uint32_t T;
-  int need;
-  bool exact;
-  uint32_t top;
-};
-
-// Given one thread's PER bin counts cb[0..PER) (its bins in descending order, the first
-// being bin `first`), finds the bin where the count from the top reaches `need` within the
-// wave whose bins these are; `before` counts everything above the wave.  Returns the
-// crossing (bin, count above it, its count), the same in every lane.  The caller
-// guarantees the crossing lies in this wave.
-template <int PER>
-__device__ __forceinline__ void wave_crossing(const int (&cb)[PER], int first, int before, int need,
-                                              int& digit, int& above, int& cnt) {
-  int local = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) local += cb[j];
-  const int incl = wave_incl_scan(local);
-  int run = before + incl - local;
-  const bool mine = run < need && run + local >= need;
-  int dj = 0, ab = 0, cn = 0;
-  bool found = false;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const bool hit = !found && run + cb[j] >= need;
-    dj = hit ? j : dj;
-    ab = hit ? run : ab;
-    cn = hit ? cb[j] : cn;
-    found = found || hit;
-    run += cb[j];
-  }
-  const int cl = (int)__builtin_ctzll(ballot(mine));
-  digit = readlane(first - dj, cl);
-  above = readlane(ab, cl);
-  cnt = readlane(cn, cl);
-}
-
-// Publishes the block's key range for find_threshold (each thread passes the min and max of
-// its own keys) and clears the histogram buffers; the caller's next barrier publishes both.
-template <int NT>
-__device__ __forceinline__ void publish_range(uint32_t lmn, uint32_t lmx, int* hist, SelState& st) {
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  lmn = wave_reduce(lmn, UMin{});
-  lmx = wave_reduce(lmx, UMax{});
-  if (lane == 0) {
-    st.wmin[w] = lmn;
-    st.wmax[w] = lmx;
-  }
-  for (int i = tid; i < kPassMax * kHistBins / 4; i += NT) reinterpret_cast<int4*>(hist)[i] = make_int4(0, 0, 0, 0);
-}
-
-// Finds the selection threshold of the top-k (1 <= k <= m) among m elements with
-// range-relative radix digits: the threshold lies in the key interval [lo, hi]; each pass
-// splits it into at most 2048 equal bins of 2^s keys (s chosen from its width), so the
-// histogram resolves wherever the keys actually are, in at most three passes.  Each pass
-// has two barriers: after the histogram, and after the per-wave totals; every wave then
-// finds the crossing wave from the totals and rescans that wave's bins itself, so the
-// result needs no broadcast.  Each pass has its own histogram buffer (cleared up front),
-// so no clearing races a slower wave's rescan.  All NT threads must call it.
-//
-// RANGED: the caller has already run publish_range (and a barrier) with every thread's key
-// range, typically while it loaded the keys, which saves a pass and a barrier.  `slack`
-// lets the search stop early, with `exact` set, once the bin holds at most `slack` more
-// elements than needed -- only for callers content with up to k + slack elements >= T.
-// The digit passes of find_threshold on the key interval [lo, hi]; fill(lo, hi, s, h) adds
-// every element whose key lies in [lo, hi] to bin (key - lo) >> s of h.
-template <int NT, class Fill>
-__device__ Threshold radix_threshold(uint32_t lo, uint32_t hi, int k, int* hist, SelState& st, int slack,
-                                     Fill&& fill) {
-  constexpr int NW = NT / WAVE;
-  constexpr int PER = kHistBins / NT;
-  static_assert(PER * NT == kHistBins, "bins per thread");
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
-  const int w = tid / WAVE;
-  const uint32_t top = hi;
-  int need = k;
-  bool exact = false;
-  for (int pass = 0; pass < kPassMax && hi != lo; ++pass) {
-    const uint32_t width = hi - lo;
-    const int s = max(0, 32 - __builtin_clz(width) - 11);
-    const int nb = (int)(width >> s) + 1;
-    int* h = hist + pass * kHistBins;
-    fill(lo, hi, s, h);
-    __syncthreads();
-    // Thread t owns bins nb-1-PER*t-j (j < PER): bins counted from the top.
-    int cb[PER];
-    int local = 0;
-    const int first = nb - 1 - PER * tid;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int b = first - j;
-      const int v = h[max(b, 0)];
-      cb[j] = b >= 0 ? v : 0;
-      local += cb[j];
-    }
-    const int incl = wave_incl_scan(local);
-    if (lane == WAVE - 1) st.wscan[w] = incl;
-    __syncthreads();
-    int before = 0, vc = -1;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const int tv = st.wscan[v];
-      const bool hit = vc < 0 && before + tv >= need;
-      before += (vc < 0 && !hit) ? tv : 0;
-      vc = hit ? v : vc;
-    }
-    // Rescan the crossing wave's bins (the same PER per lane that wave read).
-    const int first2 = nb - 1 - PER * (vc * WAVE + lane);
-    int cb2[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int b = first2 - j;
-      const int v = h[max(b, 0)];
-      cb2[j] = b >= 0 ? v : 0;
-    }
-    int d, above, cnt;
-    wave_crossing<PER>(cb2, first2, before, need, d, above, cnt);
-    need -= above;
-    const uint32_t new_lo = lo + ((uint32_t)d << s);
-    const uint64_t top_of_bin = (uint64_t)new_lo + ((uint64_t)1 << s) - 1;
-    hi = top_of_bin < (uint64_t)hi ? (uint32_t)top_of_bin : hi;
-    lo = new_lo;
-    if (cnt - need <= slack) {  // every key of the bin is taken: the selection is { key >= lo }
-      exact = true;
-      break;
-    }
-  }
-  return Threshold{lo, need, exact, top};
-}
-
-// Finds the selection threshold of the top-k (1 <= k <= m) among m elements with
-// range-relative radix digits: the threshold lies in the key interval [lo, hi]; each pass
-// splits it into at most 2048 equal bins of 2^s keys (s chosen from its width), so the
-// histogram resolves wherever the keys actually are, in at most three passes.  Each pass
-// has two barriers: after the histogram, and after the per-wave totals; every wave then
-// finds the crossing wave from the totals and rescans that wave's bins itself, so the
-// result needs no broadcast.  Each pass has its own histogram buffer (cleared up front),
-// so no clearing races a slower wave's rescan.  All NT threads must call it.
-//
-// RANGED: the caller has already run publish_range (and a barrier) with every thread's key
-// range, typically while it loaded the keys, which saves a pass and a barrier.  `slack`
-// lets the search stop early, with `exact` set, once the bin holds at most `slack` more
-// elements than needed -- only for callers content with up to k + slack elements >= T.
-template <int NT, bool RANGED = false, class Src>
-__device__ Threshold find_threshold(const Src& src, int m, int k, int* hist, SelState& st,
-                                    int slack = 0) {
-  constexpr int NW = NT / WAVE;
-  if (!RANGED) {
-    uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
-    for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
-      lmn = min(lmn, key);
-      lmx = max(lmx, key);
-    });
-    publish_range<NT>(lmn, lmx, hist, st);
-    __syncthreads();
-  }
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    lo = min(lo, st.wmin[i]);
-    hi = max(hi, st.wmax[i]);
-  }
-  return radix_threshold<NT>(lo, hi, k, hist, st, slack, [&](uint32_t a, uint32_t b, int s, int* h) {
-    for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
-      if (key >= a && key <= b) atomicAdd(&h[(key - a) >> s], 1);
-    });
-  });
-}
-
-// Writes the ids of the selected elements, in ascending position order, to out[0..k).
-// Each wave walks a contiguous position range with ballots, so elements equal to T are
-// taken lowest position first; the waves' output offsets come from two DPP scans over
-// the per-wave counts.  Predicates combine with bitwise operators so the element loop is
-// straight-line mask arithmetic, and ids are read together with keys, before any is used.
-template <int NT, class Src>
-__device__ void emit_selected(const Src& src, int m, const Threshold& th, SelState& st,
-                              int32_t* __restrict__ out) {
-  constexpr int NW = NT / WAVE;
-  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  const uint32_t T = th.T;
-  const bool ex = th.exact;
-  const int need = ex ? 0 : th.need;
-  const int per = ((m + NW - 1) / NW + WAVE - 1) / WAVE * WAVE;
-  const int beg = w * per;
-  const int end = min(m, beg + per);
-  constexpr int U = 8;  // rounds of 64 whose keys are read before they are used
-  int cgt = 0, ceq = 0;
-  for (int i0 = beg; i0 < end; i0 += U * WAVE) {
-    uint32_t kv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) kv[u] = src.key(min(i0 + u * WAVE + lane, end - 1));
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool in = i0 + u * WAVE + lane < end;
-      cgt += __popcll(ballot(in & ((kv[u] > T) | (ex & (kv[u] == T)))));
-      ceq += __popcll(ballot(in & !ex & (kv[u] == T)));
-    }
-  }
-  if (lane == 0) {
-    st.wtot[0][w] = cgt;
-    st.wtot[1][w] = ceq;
-  }
-  __syncthreads();
-  // Lane v < NW stands for wave v: ties are taken in wave order until `need` is met.
-  const int gt_v = lane < NW ? st.wtot[0][lane] : 0;
-  const int eq_v = lane < NW ? st.wtot[1][lane] : 0;
-  const int eq_before_v = wave_incl_scan(eq_v) - eq_v;
-  const int take_v = min(max(need - eq_before_v, 0), eq_v);
-  const int sel_v = gt_v + take_v;
-  const int sel_before_v = wave_incl_scan(sel_v) - sel_v;
-  const int eq_before = readlane(eq_before_v, w);
-  const int sel_before = readlane(sel_before_v, w);
-  int eq_run = 0, sel_run = 0;
-  for (int i0 = beg; i0 < end; i0 += U * WAVE) {
-    uint32_t kv[U];
-    int iv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = min(i0 + u * WAVE + lane, end - 1);
-      kv[u] = src.key(e);
-      iv[u] = src.id(e);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool in = i0 + u * WAVE + lane < end;
-      const bool gt = in & ((kv[u] > T) | (ex & (kv[u] == T)));
-      const bool eq = in & !ex & (kv[u] == T);
-      const uint64_t eqm = ballot(eq);
-      const bool sel = gt | (eq & (eq_before + eq_run + mask_rank(eqm) < need));
-      const uint64_t selm = ballot(sel);
-      if (sel) out[sel_before + sel_run + mask_rank(selm)] = iv[u];
-      eq_run += __popcll(eqm);
-      sel_run += __popcll(selm);
-    }
-  }
-}
 
 // Long rows, pass 1 (R x chunks workgroups): every workgroup of a row derives the same
-// sample threshold theta -- the ks-th largest of kSample evenly spaced scores, ks chosen
-// so that ~2k scores of the row are expected to reach it -- while the loads of its own
-// 4096-score chunk are in flight, then compacts the chunk's survivors (key >= theta) in
-// index order into the chunk's slot of the candidate buffer and records their count.
-// Chunk 0 also records theta and the survivor-bin shift for the resolve.
-// With `gsamp` (the fused index + top-k call) the sample comes contiguously from gsamp[r, :],
-// which the indexer filled with the scores at the same positions.  n = n_valid[r] + n_off.
+// sample threshold theta (about 2k survivors expected) from kSample evenly spaced scores
+// (positions (i * n) / kSample)
+// while the loads of its own 4096-score chunk are in flight, then compacts the chunk's
+// survivors (key >= theta) in index order into the chunk's slot of the candidate buffer and
+// records how many of them lie above theta and how many equal it.  Chunk 0 also records the
+// row header for the resolve.  n = n_valid[r] + n_off.
 __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
-    RowHeader* __restrict__ hdr, uint32_t* __restrict__ counts, int max_chunks,
-    uint2* __restrict__ cand, const float* __restrict__ gsamp, int n_off, int long_min) {
+    RowHeader* __restrict__ hdr, ChunkCount* __restrict__ counts, int max_chunks,
+    uint2* __restrict__ cand, int n_off, int long_min) {
   __shared__ uint32_t samp[kSample];
   __shared__ __attribute__((aligned(16))) int hist[kPassMax * kHistBins];
   __shared__ SelState st;
@@ -419,62 +94,42 @@ __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
     const int e = wb + it * WAVE + lane;
     key[it] = float_key(row[min(e, end - 1)]);  // unconditional: all loads in flight at once
   }
+  uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
   {
     constexpr int kPer = kSample / kLongThreads;
     uint32_t kv[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      kv[u] = float_key(gsamp ? gsamp[(int64_t)r * kSample + tid + u * kLongThreads]
-                              : row[(int64_t)(tid + u * kLongThreads) * n / kSample]);
-    uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
+    for (int u = 0; u < kPer; ++u) kv[u] = float_key(row[(int64_t)(tid + u * kLongThreads) * n / kSample]);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       samp[tid + u * kLongThreads] = kv[u];
       lmn = min(lmn, kv[u]);
       lmx = max(lmx, kv[u]);
     }
-    publish_range<kLongThreads>(lmn, lmx, hist, st);
   }
-  __syncthreads();
-  int ks = (int)(((int64_t)2 * k * kSample + n - 1) / n);
-  ks = ks < 1 ? 1 : (ks > kSample ? kSample : ks);
-  // Any sample key of rank ks .. ks + ks/4 serves: the search stops at the first bin that
-  // close, usually after one pass.
-  const Threshold th = find_threshold<kLongThreads, true>(LdsKeys{samp, 0}, kSample, ks, hist, st, ks / 4);
-  // theta = the smallest sample key >= T.  (When the search stops early T is only that
-  // bin's lower bound, and the full row can hold many more scores between T and the
-  // smallest sample in the bin.)
-  uint32_t theta = th.T;
-  if (th.exact) {
-    uint32_t mn = 0xFFFFFFFFu;
-    for (int i = tid; i < kSample; i += kLongThreads) {
-      const uint32_t sk = samp[i];
-      if (sk >= th.T) mn = min(mn, sk);
-    }
-    mn = wave_reduce(mn, UMin{});
-    if (lane == 0) st.wred[w] = mn;  // not wmin: slower waves may still read that
-    __syncthreads();
-    theta = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) theta = min(theta, st.wred[i]);
-  }
-  if (c == 0 && tid == 0) {
-    // Survivor bins span [theta, largest sample] in at most kSurvBins steps of 2^shift;
-    // scores above the largest sample land in the last bin.
-    const uint32_t width = th.top - theta;
-    const int shift = width ? max(0, 32 - __builtin_clz(width) - 12) : 0;
-    hdr[r] = RowHeader{theta, (uint32_t)shift};
-  }
-  int cnt = 0;
+  const RowHeader rh = sample_header<kLongThreads>(samp, kSample, 2, lmn, lmx, n, k, hist, st);
+  const uint32_t theta = rh.theta;
+  if (c == 0 && tid == 0) hdr[r] = rh;
+  int gt = 0, eq = 0;
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
-    const int e = wb + it * WAVE + lane;
-    cnt += __popcll(ballot(e < end && key[it] >= theta));
+    const bool in = wb + it * WAVE + lane < end;
+    gt += __popcll(ballot(in & (key[it] > theta)));
+    eq += __popcll(ballot(in & (key[it] == theta)));
   }
-  if (lane == 0) st.wtot[0][w] = cnt;
+  if (lane == 0) {
+    st.wtot[0][w] = gt;
+    st.wtot[1][w] = eq;
+  }
   __syncthreads();
-  int off = 0;
-  for (int v = 0; v < w; ++v) off += st.wtot[0][v];
+  int off = 0, G = 0, E = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const int a = st.wtot[0][v], b = st.wtot[1][v];
+    off += v < w ? a + b : 0;
+    G += a;
+    E += b;
+  }
   uint2* cr = cand + (int64_t)r * ld + base;
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
@@ -484,7 +139,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
     if (keep) cr[off + mask_rank(km)] = make_uint2(key[it], (uint32_t)e);
     off += __popcll(km);
   }
-  if (tid == kLongThreads - 1) counts[(int64_t)r * max_chunks + c] = (uint32_t)off;
+  if (tid == 0) counts[(int64_t)r * max_chunks + c] = ChunkCount{(uint32_t)G, (uint32_t)E, theta, 0u};
 }
 
 // Exact top-k among `total` survivors (keys/ids in LDS, in index order) that all lie at or
@@ -621,7 +276,7 @@ __device__ __forceinline__ void select_survivors(const uint32_t* keys, const int
 // to the last element) so they all issue back to back; a branch around each would make the
 // compiler wait for each in turn.
 template <int KPT>
-__device__ void select_mid_row(const float* __restrict__ row, int n, int k, int32_t* __restrict__ out,
+__device__ __forceinline__ void select_mid_row(const float* __restrict__ row, int n, int k, int32_t* __restrict__ out,
                                int* hist, SelState& st) {
   constexpr int NT = kRowThreads, NW = NT / WAVE;
   static_assert(KPT * NT <= kRowMax, "keys per thread");
@@ -698,24 +353,130 @@ __device__ void select_mid_row(const float* __restrict__ row, int n, int k, int3
   }
 }
 
-// Long rows, pass 2 (one workgroup per row): exact top-k among the survivors in LDS, or
-// among the whole row when the sample threshold kept fewer than k or more than fit.  The
-// survivors are histogrammed into kSurvBins bins above theta as they are gathered, so the
-// bin holding the k-th largest is found by one block scan; the keys of that bin are then
-// ranked directly, or by the radix select when there are too many of them.
-__device__ void resolve_long_row(const float* __restrict__ row, int ld, int n, int k, int r,
-                                 int32_t* __restrict__ out, const RowHeader* __restrict__ hdr,
-                                 const uint32_t* __restrict__ counts, int max_chunks,
-                                 const uint2* __restrict__ cand, uint32_t* smem, int* hist,
-                                 uint2* ties, SelState& st) {
+// Inputs of the indexer's fast shape, for the fused call's sample pass and its rescoring
+// fallback (the same scoring core as the indexer: score_core.h).
+struct Rescore {
+  const uint8_t* q;        // [R, 64, 128] e4m3 codes
+  const float* q_scale;    // [R] or null
+  const float* w;          // [R, 64]
+  const uint8_t* kdata;    // key cache, 128 bytes per row
+  const float* kscale;     // per-row key scale or null
+  KeyRows kr;
+  const int32_t* row_seq;  // [R]
+};
+
+// Scores positions 0 .. n-1 of row r into order-preserving keys keys_out[0 .. n) (all threads
+// of the block; the caller publishes them with a barrier).
+__device__ void rescore_row(const Rescore& rs, int r, int n, uint32_t* __restrict__ keys_out) {
+  constexpr int NW = kResolveThreads / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int col = lane & 15, grp = lane >> 4;
+  v8i qa[4];
+  float wr[4][4];
+  load_query(rs.q + (int64_t)r * (64 * 128), rs.w + (int64_t)r * 64, col, grp, qa, wr);
+  const float qs = rs.q_scale ? rs.q_scale[r] : 1.0f;
+  const int seq = rs.row_seq[r];
+  const int ntrips = (n + kIdxBatch - 1) / kIdxBatch;
+  for (int t = w; t < ntrips; t += NW) {
+    const int s0 = t * kIdxBatch;
+    v8i kb[4];
+    load_trip(rs.kdata, rs.kr, seq, col, grp, [&](int j) { return (int64_t)min(s0 + j, n - 1); }, kb);
+    const float ks = rs.kscale ? rs.kscale[rs.kr.row(seq, min(s0 + lane, n - 1))] : 1.0f;
+    const float sc = scaled_score(trip_scores(qa, wr, kb), ks, qs);
+    if (s0 + lane < n) keys_out[s0 + lane] = float_key(sc);
+  }
+}
+
+// Theta is the threshold itself: fewer than k keys above theta (G of them) and at least k at
+// or above it.  Every key above theta is kept, and the first k - G keys equal to theta in
+// position order.  Chunk j keeps its keys above theta and eqt_j of its keys equal to theta
+// (those before it have taken pe[j]), from output offset pg[j] + min(pe[j], k - G).  When a
+// chunk keeps a prefix of its slot -- it has no key equal to theta, or keeps all of them, or
+// has only such keys -- its ids are copied straight out: output position p finds its chunk
+// by binary search over the offsets.  Any other chunk is walked by one wave with ballots.
+__device__ void emit_theta_boundary(const uint2* __restrict__ rcand, int C, int nch, const int* pg,
+                                    const int* pe, uint32_t theta, int k, int32_t* __restrict__ out) {
+  constexpr int NW = kResolveThreads / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int G = pg[nch];
+  const int take = k - G;
+  auto sb = [&](int j) { return pg[j] + min(pe[j], take); };
+  auto eqt = [&](int j) { return min(max(take - pe[j], 0), pe[j + 1] - pe[j]); };
+  auto direct = [&](int j) {
+    const int g = pg[j + 1] - pg[j], e = pe[j + 1] - pe[j];
+    return g == 0 || e == 0 || eqt(j) == e;
+  };
+  constexpr int U = 4;
+  for (int p0 = 0; p0 < k; p0 += U * kResolveThreads) {
+    int src[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * kResolveThreads + tid;
+      src[u] = -1;
+      if (p < k) {
+        int lo = 0, hi = nch - 1;  // the last chunk whose offset is <= p
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sb(mid) <= p) lo = mid; else hi = mid - 1;
+        }
+        if (direct(lo)) src[u] = lo * C + (p - sb(lo));
+      }
+    }
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[u] >= 0 ? (int)rcand[src[u]].y : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (src[u] >= 0) out[p0 + u * kResolveThreads + tid] = v[u];
+  }
+  for (int j = w; j < nch; j += NW) {
+    const int g = pg[j + 1] - pg[j];
+    const int et = eqt(j);
+    if (direct(j) || g + et == 0) continue;
+    const int cnt = g + (pe[j + 1] - pe[j]);
+    const uint2* cj = rcand + (int64_t)j * C;
+    int eq_run = 0, sel_run = sb(j);
+    for (int i0 = 0; i0 < cnt; i0 += U * WAVE) {
+      uint2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = cj[min(i0 + u * WAVE + lane, cnt - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = i0 + u * WAVE + lane < cnt;
+        const bool eq = ok & (v[u].x == theta);
+        const uint64_t eqm = ballot(eq);
+        const bool sel = (ok & (v[u].x > theta)) | (eq & (eq_run + mask_rank(eqm) < et));
+        const uint64_t selm = ballot(sel);
+        if (sel) out[sel_run + mask_rank(selm)] = (int)v[u].y;
+        eq_run += __popcll(eqm);
+        sel_run += __popcll(selm);
+      }
+    }
+  }
+}
+
+// Long rows, pass 2 (one workgroup per row).  The chunks' survivor counts give, by one scan,
+// how many keys lie above theta (G) and at it (E); then the three cases of the file comment.
+// C is the chunk length of the candidate slots; `row` is the score row, or null in the fused
+// call, whose fallback rescores the row (through rs) into its candidate slots first.
+// kPre x U: chunks per wave and slot rounds per chunk loaded before the counts are known
+// (sized to the launch's chunks: ~4k survivors in 32 chunks of 4096 positions, or ~6k in 64
+// chunks of 2048).
+template <int kPre, int U>
+__device__ void resolve_long_row(const float* __restrict__ row, const Rescore& rs, int64_t ld, int n, int k,
+                                 int r, int32_t* __restrict__ out, const RowHeader* __restrict__ hdr,
+                                 const ChunkCount* __restrict__ counts, int max_chunks, int C,
+                                 uint2* __restrict__ cand, uint64_t* __restrict__ ready, uint32_t* smem,
+                                 int* hist, uint2* ties, SelState& st) {
   static_assert(kSurvBins <= kPassMax * kHistBins, "the survivor histogram reuses the radix buffers");
   static_assert(kSurvBins == 4 * kResolveThreads, "four survivor bins per thread");
   constexpr int NW = kResolveThreads / WAVE;
-  const int nch = (n + kChunk - 1) / kChunk;
+  const int nch = (n + C - 1) / C;
   uint32_t* keys = smem;
   int* ids = reinterpret_cast<int*>(smem + kCandCap);
-  int* offs = reinterpret_cast<int*>(smem + 2 * kCandCap);
-  const uint32_t* rc = counts + (int64_t)r * max_chunks;
+  int* pg = reinterpret_cast<int*>(smem + 2 * kCandCap);  // [nch + 1] survivors above theta before chunk j
+  int* pe = pg + max_chunks + 1;                          // [nch + 1] survivors equal to theta before chunk j
+  const ChunkCount* rc = counts + (int64_t)r * max_chunks;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const RowHeader rh = hdr[r];
   // The first 64 chunk counts (wave 0), then -- before any count is known -- the first
@@ -723,46 +484,71 @@ __device__ void resolve_long_row(const float* __restrict__ row, int ld, int n, i
   // hold stale pairs and are dropped below).  The count load goes first, so waiting for it
   // leaves the candidate loads in flight, and a typical row's gather costs the one round
   // trip these loads share.
-  constexpr int U = 4, kPre = 2;
-  const uint2* rcand = cand + (int64_t)r * ld;
-  const int c0 = (w == 0 && lane < nch) ? (int)rc[lane] : 0;
+  uint2* rcand = cand + (int64_t)r * ld;
+  const ChunkCount c0 = (w == 0 && lane < nch) ? rc[lane] : ChunkCount{0u, 0u, rh.theta, 0u};
+  if (ready && tid == 0) ready[r] = 0;  // the next call's scoring blocks wait for a fresh threshold
   uint2 pre[kPre][U];
 #pragma unroll
   for (int m = 0; m < kPre; ++m) {
     const int j = w + m * NW < nch ? w + m * NW : 0;
-    const int cl = min(kChunk, n - j * kChunk);  // the chunk's length: slots stay in the row
+    const int cl = min(C, n - j * C);  // the chunk's length: slots stay in the row
 #pragma unroll
-    for (int u = 0; u < U; ++u) pre[m][u] = rcand[(int64_t)j * kChunk + min(u * WAVE + lane, cl - 1)];
+    for (int u = 0; u < U; ++u) pre[m][u] = rcand[(int64_t)j * C + min(u * WAVE + lane, cl - 1)];
   }
-  if (w == 0) {  // exclusive prefix of the survivor counts, 64 chunks per step
-    int carry = 0;
+  if (w == 0) {  // exclusive prefixes of the survivor counts, 64 chunks per step
+    int cg = 0, ce = 0;
+    bool stale = false;  // a chunk compacted with another threshold than the row's
     for (int j0 = 0; j0 < nch; j0 += WAVE) {
       const int j = j0 + lane;
-      const int cj = j0 == 0 ? c0 : (j < nch ? (int)rc[j] : 0);
-      const int incl = wave_incl_scan(cj);
-      if (j < nch) offs[j] = carry + incl - cj;
-      carry += __shfl(incl, WAVE - 1);
+      const ChunkCount cj = j0 == 0 ? c0 : (j < nch ? rc[j] : ChunkCount{0u, 0u, rh.theta, 0u});
+      stale = stale || cj.theta != rh.theta;
+      const int ig = wave_incl_scan((int)cj.gt), ie = wave_incl_scan((int)cj.eq);
+      if (j < nch) {
+        pg[j] = cg + ig - (int)cj.gt;
+        pe[j] = ce + ie - (int)cj.eq;
+      }
+      cg += __shfl(ig, WAVE - 1);
+      ce += __shfl(ie, WAVE - 1);
     }
-    if (lane == 0) offs[nch] = carry;
+    if (lane == 0) {
+      pg[nch] = ballot(stale) ? -1 : cg;  // -1: the survivors are not one threshold's
+      pe[nch] = ce;
+    }
   }
   reinterpret_cast<int4*>(hist)[tid] = make_int4(0, 0, 0, 0);
   if (tid == 0) st.ntie = 0;
   __syncthreads();
-  const int total = offs[nch];
+  const int G = pg[nch];
+  const int total = G < 0 ? -1 : G + pe[nch];
+  if (G >= 0 && G < k && k <= total) {
+    emit_theta_boundary(rcand, C, nch, pg, pe, rh.theta, k, out);
+    return;
+  }
   if (total < k || total > kCandCap) {
-    const GlobalRow src{row};
-    const Threshold th = find_threshold<kResolveThreads>(src, n, k, hist, st);
-    emit_selected<kResolveThreads>(src, n, th, st, out);
+    if (row) {
+      const GlobalRow src{row};
+      const Threshold th = find_threshold<kResolveThreads>(src, n, k, hist, st);
+      emit_selected<kResolveThreads>(src, n, th, st, out);
+    } else {
+      // The row's candidate slots (8 bytes per position) hold its n keys from here on.
+      uint32_t* rk = reinterpret_cast<uint32_t*>(rcand);
+      rescore_row(rs, r, n, rk);
+      __syncthreads();
+      const GlobalKeys src{rk};
+      const Threshold th = find_threshold<kResolveThreads>(src, n, k, hist, st);
+      emit_selected<kResolveThreads>(src, n, th, st, out);
+    }
     return;
   }
   {
     // Wave w copies chunks w, w + NW, ...: the preloaded slots first, then (for chunks
     // with more survivors, or beyond the first kPre) U loads per lane per round trip.
+    auto off = [&](int j) { return pg[j] + pe[j]; };
 #pragma unroll
     for (int m = 0; m < kPre; ++m) {
       const int j = w + m * NW;
       if (j < nch) {
-        const int o = offs[j], cj = min(offs[j + 1] - o, U * WAVE);
+        const int o = off(j), cj = min(off(j + 1) - o, U * WAVE);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int i = u * WAVE + lane;
@@ -775,11 +561,11 @@ __device__ void resolve_long_row(const float* __restrict__ row, int ld, int n, i
       }
     }
     for (int j = w; j < nch; j += NW) {
-      const int o = offs[j], cj = offs[j + 1] - o;
+      const int o = off(j), cj = off(j + 1) - o;
       for (int i0 = j < w + kPre * NW ? U * WAVE : 0; i0 < cj; i0 += U * WAVE) {
         uint2 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = rcand[(int64_t)j * kChunk + min(i0 + u * WAVE + lane, cj - 1)];
+        for (int u = 0; u < U; ++u) v[u] = rcand[(int64_t)j * C + min(i0 + u * WAVE + lane, cj - 1)];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int i = i0 + u * WAVE + lane;
@@ -797,10 +583,13 @@ __device__ void resolve_long_row(const float* __restrict__ row, int ld, int n, i
 }
 
 // One workgroup per row: trivial rows, LDS-resident rows, or the resolve of long rows.
+// scores == null (the fused call): every row longer than k takes the resolve.
+template <int kPre, int U>
 __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
-    int32_t* __restrict__ idx, const RowHeader* __restrict__ hdr, const uint32_t* __restrict__ counts,
-    int max_chunks, const uint2* __restrict__ cand, int n_off, int long_min) {
+    int32_t* __restrict__ idx, const RowHeader* __restrict__ hdr, const ChunkCount* __restrict__ counts,
+    int max_chunks, int chunk, uint2* __restrict__ cand, uint64_t* __restrict__ ready, int n_off, int long_min,
+    Rescore rs) {
   static_assert(kRowThreads == kResolveThreads, "one kernel serves both paths");
   extern __shared__ uint32_t smem[];  // long rows: survivor keys, ids and chunk offsets
   __shared__ __attribute__((aligned(16))) int hist[kPassMax * kHistBins];
@@ -811,35 +600,47 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
   n64 = n64 < 0 ? 0 : (n64 > ld ? ld : n64);
   const int n = (int)n64;
   int32_t* out = idx + (int64_t)r * k;
-  const float* row = scores + (int64_t)r * ld;
+  const float* row = scores ? scores + (int64_t)r * ld : nullptr;
   if (n <= k) {
     for (int i = threadIdx.x; i < k; i += kRowThreads) out[i] = i < n ? i : -1;
     return;
   }
-  if (n <= long_min) {
+  if (row && n <= long_min) {
     if (n <= kRowMax / 4) select_mid_row<kRowMax / 4 / kRowThreads>(row, n, k, out, hist, st);
     else if (n <= kRowMax / 2) select_mid_row<kRowMax / 2 / kRowThreads>(row, n, k, out, hist, st);
     else select_mid_row<kRowMax / kRowThreads>(row, n, k, out, hist, st);
     return;
   }
-  resolve_long_row(row, (int)ld, n, k, r, out, hdr, counts, max_chunks, cand, smem, hist, ties, st);
+  resolve_long_row<kPre, U>(row, rs, ld, n, k, r, out, hdr, counts, max_chunks, chunk, cand, ready, smem, hist,
+                            ties, st);
 }
 
 struct WsLayout {
-  size_t hdr, counts, cand, total;
+  size_t ready, hdr, counts, cand, total;
   int max_chunks;
 };
 
-WsLayout ws_layout(int R, int64_t ld) {
+// [ready [R] (fused call only)], hdr [R], counts [R, max_chunks], cand [R, ld] (one 8-byte
+// slot per position).
+WsLayout long_ws(int R, int64_t ld, int chunk, bool fused) {
   WsLayout L{};
-  if (ld <= kRowMax) return L;
-  L.max_chunks = (int)((ld + kChunk - 1) / kChunk);
+  L.max_chunks = (int)((ld + chunk - 1) / chunk);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  L.hdr = 0;
-  L.counts = up(sizeof(RowHeader) * (size_t)R);
-  L.cand = L.counts + up(sizeof(uint32_t) * (size_t)R * L.max_chunks);
+  L.ready = 0;
+  L.hdr = fused ? up(sizeof(uint64_t) * (size_t)R) : 0;
+  L.counts = L.hdr + up(sizeof(RowHeader) * (size_t)R);
+  L.cand = L.counts + up(sizeof(ChunkCount) * (size_t)R * L.max_chunks);
   L.total = L.cand + up(sizeof(uint2) * (size_t)R * (size_t)ld);
   return L;
+}
+
+WsLayout ws_layout(int R, int64_t ld) {
+  if (ld <= kRowMax) return WsLayout{};
+  return long_ws(R, ld, kChunk, false);
+}
+
+size_t finish_lds_bytes(int max_chunks) {
+  return sizeof(uint32_t) * (2 * (size_t)kCandCap + 2 * ((size_t)max_chunks + 1));
 }
 
 }  // namespace
@@ -856,23 +657,54 @@ size_t topk_workspace_bytes(int R, int64_t ld, int k) {
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
-                       int32_t* idx, void* ws, hipStream_t s, const float* samp, int n_off) {
+                       int32_t* idx, void* ws, hipStream_t s, int n_off) {
   const WsLayout L = ws_layout(R, ld);
   const int long_min = topk_long_row_min(ld);
   char* wsb = static_cast<char*>(ws);
   RowHeader* hdr = L.total ? reinterpret_cast<RowHeader*>(wsb + L.hdr) : nullptr;
-  uint32_t* counts = L.total ? reinterpret_cast<uint32_t*>(wsb + L.counts) : nullptr;
+  ChunkCount* counts = L.total ? reinterpret_cast<ChunkCount*>(wsb + L.counts) : nullptr;
   uint2* cand = L.total ? reinterpret_cast<uint2*>(wsb + L.cand) : nullptr;
   if (L.total) {
     topk_prep_kernel<<<(unsigned)R * (unsigned)L.max_chunks, kLongThreads, 0, s>>>(
-        scores, ld, n_valid, k, hdr, counts, L.max_chunks, cand, samp, n_off, long_min);
+        scores, ld, n_valid, k, hdr, counts, L.max_chunks, cand, n_off, long_min);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // Long rows: survivor keys and ids, then the chunk offsets (rows up to kRowMax need none).
-  const size_t lds = L.total ? sizeof(uint32_t) * (2 * (size_t)kCandCap + L.max_chunks + 1) : 0;
-  topk_finish_kernel<<<R, kRowThreads, lds, s>>>(
-      scores, ld, n_valid, k, idx, hdr, counts, L.max_chunks, cand, n_off, long_min);
+  const size_t lds = L.total ? finish_lds_bytes(L.max_chunks) : 0;
+  topk_finish_kernel<2, 4><<<R, kRowThreads, lds, s>>>(scores, ld, n_valid, k, idx, hdr, counts, L.max_chunks,
+                                                       kChunk, cand, nullptr, n_off, long_min, Rescore{});
+  return hipGetLastError();
+}
+
+// ---- fused index + top-k (fast indexer shape)
+
+size_t index_topk_fused_bytes(int R, int64_t ld) { return long_ws(R, ld, index_keys_per_wg(R, ld), true).total; }
+
+bool index_topk_fused_ok(int R, int64_t ld) {
+  const int mc = long_ws(R, ld, index_keys_per_wg(R, ld), true).max_chunks;
+  return mc <= kFusedMaxChunks && (int64_t)R * (mc + 1) <= 2147483647LL;
+}
+
+hipError_t launch_index_topk_fused(const uint8_t* q, const float* q_scale, const float* w, const CacheView& keys,
+                                   const int32_t* row_seq, const int32_t* row_pos, int R, int64_t ld, int k,
+                                   int32_t* idx, void* ws, hipStream_t s) {
+  const int chunk = index_keys_per_wg(R, ld);
+  const WsLayout L = long_ws(R, ld, chunk, true);
+  char* wsb = static_cast<char*>(ws);
+  uint64_t* ready = reinterpret_cast<uint64_t*>(wsb + L.ready);
+  RowHeader* hdr = reinterpret_cast<RowHeader*>(wsb + L.hdr);
+  ChunkCount* counts = reinterpret_cast<ChunkCount*>(wsb + L.counts);
+  uint2* cand = reinterpret_cast<uint2*>(wsb + L.cand);
+  const int ps = keys.table ? keys.page_size : 1;
+  const int shift = keys.table && (ps & (ps - 1)) == 0 ? __builtin_ctz(ps) : -1;
+  const Rescore rs{q, q_scale, w, static_cast<const uint8_t*>(keys.data), keys.scale,
+                   KeyRows{keys.table, keys.max_pages, ps, shift, keys.seq_stride}, row_seq};
+  hipError_t e = launch_index_fp8_compact(q, q_scale, w, keys, row_seq, row_pos, R, ld, ld, hdr, ready, counts, cand,
+                                          k, s);
+  if (e != hipSuccess) return e;
+  topk_finish_kernel<4, 2><<<R, kRowThreads, finish_lds_bytes(L.max_chunks), s>>>(
+      nullptr, ld, row_pos, k, idx, hdr, counts, L.max_chunks, chunk, cand, ready, 1, 0, rs);
   return hipGetLastError();
 }
 

@@ -4,10 +4,12 @@ The pages' order -- an FP8 indexer first, then the top-k choice, then core atten
 the chosen tokens only
 (MarkTechPost, "DeepSeek V3.2-Exp Cuts Long-Context Costs with DeepSeek Sparse
 Attention (DSA) ...") -- run as dsa_index_scores -> dsa_topk -> dsa_sparse_mla_*.
-These classes only own the intermediate buffers (score rows, kept indices,
-workspaces, outputs; allocated once, at construction) and issue the calls in order.
-A decode step runs the first two as the one call dsa_index_topk (same result);
-index() and topk() issue them separately, for per-stage timing.
+These classes only own the intermediate buffers (kept indices, workspaces, outputs;
+allocated once, at construction) and issue the calls in order.  run() issues the first
+two as the one call dsa_index_topk (same result as the two calls), which at decode stores
+no score row and at prefill scores a bounded block of rows at a time; index() and topk()
+issue the two calls separately into a full score buffer, for per-stage timing and
+diagnostics -- that buffer ([B, ld] at decode, [T, T] at prefill) is allocated on first use.
 """
 from __future__ import annotations
 
@@ -41,14 +43,12 @@ class DecodeStep:
         self.idx_dt = F32 if fp32 else E4M3
         self.mla_dt = F32 if fp32 else BF16
         fw = dsa_index_topk_workspace_size(self.B, self.ld, self.k)
-        self.fused_ws = torch.empty(max(fw, 1), dtype=torch.uint8, device=dev)
+        # zeroed once: the fused call's hand-off words start clear (any contents are correct)
+        self.fused_ws = torch.zeros(max(fw, 1), dtype=torch.uint8, device=dev)
         self.fused_ws_bytes = fw
-        # the fused call leaves the scores [B, ld] at the start of its workspace
-        self.scores = self.fused_ws[: self.B * self.ld * 4].view(torch.float32).view(self.B, self.ld)
         self.idx = torch.empty(self.B, self.k, dtype=torch.int32, device=dev)
-        tw = dsa_topk_workspace_size(self.B, self.ld, self.k)
-        self.topk_ws = torch.empty(max(tw, 1), dtype=torch.uint8, device=dev)
-        self.topk_ws_bytes = tw
+        self._scores = None
+        self._topk_ws = None
         odt = torch.float32 if fp32 else torch.bfloat16
         self.out = torch.empty(self.B, self.H, self.Dv, dtype=odt, device=dev)
         self.lse = torch.empty(self.B, self.H, dtype=torch.float32, device=dev)
@@ -65,13 +65,28 @@ class DecodeStep:
                    softmax_scale=softmax_scale, Dv=Dv, block_table=d.block_table,
                    page_size=d.page_size, seq_stride=d.seq_stride, fp32=fp32)
 
+    @property
+    def scores(self):
+        """Score rows [B, ld] of index() (allocated on first use; run() never touches them)."""
+        if self._scores is None:
+            self._scores = torch.empty(self.B, self.ld, dtype=torch.float32, device=self.q.device)
+        return self._scores
+
+    @property
+    def topk_ws(self):
+        if self._topk_ws is None:
+            tw = dsa_topk_workspace_size(self.B, self.ld, self.k)
+            self._topk_ws = (torch.empty(max(tw, 1), dtype=torch.uint8, device=self.q.device), tw)
+        return self._topk_ws
+
     def index(self, stream=None):
         dsa_index_scores(self.idx_dt, self.q_idx, self.q_scale, self.w, self.keys, self.row_seq,
                          self.row_pos, self.B, self.HI, self.dI, self.scores, self.ld, stream)
 
-    def topk(self, stream=None):
-        dsa_topk(self.scores, self.ld, self.n_valid, self.B, self.k, self.idx, self.topk_ws,
-                 self.topk_ws_bytes, stream)
+    def topk(self, stream=None, out=None):
+        ws, wb = self.topk_ws
+        dsa_topk(self.scores, self.ld, self.n_valid, self.B, self.k, self.idx if out is None else out,
+                 ws, wb, stream)
 
     def index_topk(self, stream=None):
         dsa_index_topk(self.idx_dt, self.q_idx, self.q_scale, self.w, self.keys, self.row_seq,
@@ -110,29 +125,49 @@ class Prefill:
         self.keys = Cache(keys, k_scale, None, 0, self.T)
         self.idx_dt = F32 if fp32 else E4M3
         self.mla_dt = F32 if fp32 else BF16
-        self.scores = torch.empty(self.T, self.T, dtype=torch.float32, device=dev)
         self.idx = torch.empty(self.T, self.k, dtype=torch.int32, device=dev)
-        tw = dsa_topk_workspace_size(self.T, self.T, self.k)
-        self.topk_ws = torch.empty(max(tw, 1), dtype=torch.uint8, device=dev)
-        self.topk_ws_bytes = tw
+        fw = dsa_index_topk_workspace_size(self.T, self.T, self.k)
+        self.fused_ws = torch.zeros(max(fw, 1), dtype=torch.uint8, device=dev)
+        self.fused_ws_bytes = fw
+        self._scores = None
+        self._topk_ws = None
         odt = torch.float32 if fp32 else torch.bfloat16
         self.out = torch.empty(self.T, self.H, self.Dv, dtype=odt, device=dev)
         self.lse = torch.empty(self.T, self.H, dtype=torch.float32, device=dev)
+
+    @property
+    def scores(self):
+        """The [T, T] score matrix of index() (allocated on first use; run() never needs it)."""
+        if self._scores is None:
+            self._scores = torch.empty(self.T, self.T, dtype=torch.float32, device=self.q.device)
+        return self._scores
+
+    @property
+    def topk_ws(self):
+        if self._topk_ws is None:
+            tw = dsa_topk_workspace_size(self.T, self.T, self.k)
+            self._topk_ws = (torch.empty(max(tw, 1), dtype=torch.uint8, device=self.q.device), tw)
+        return self._topk_ws
 
     def index(self, stream=None):
         dsa_index_scores(self.idx_dt, self.q_idx, self.q_scale, self.w, self.keys, self.row_seq,
                          self.row_pos, self.T, self.HI, self.dI, self.scores, self.T, stream)
 
-    def topk(self, stream=None):
-        dsa_topk(self.scores, self.T, self.n_valid, self.T, self.k, self.idx, self.topk_ws,
-                 self.topk_ws_bytes, stream)
+    def topk(self, stream=None, out=None):
+        ws, wb = self.topk_ws
+        dsa_topk(self.scores, self.T, self.n_valid, self.T, self.k, self.idx if out is None else out,
+                 ws, wb, stream)
+
+    def index_topk(self, stream=None):
+        dsa_index_topk(self.idx_dt, self.q_idx, self.q_scale, self.w, self.keys, self.row_seq,
+                       self.row_pos, self.T, self.HI, self.dI, self.k, self.idx, self.fused_ws,
+                       self.fused_ws_bytes, stream)
 
     def attend(self, stream=None):
         dsa_sparse_mla_prefill(self.mla_dt, self.q, self.kvt, self.idx, self.T, self.H, self.Dqk,
                                self.Dv, self.k, self.scale, self.out, self.lse, stream)
 
     def run(self, stream=None):
-        self.index(stream)
-        self.topk(stream)
+        self.index_topk(stream)
         self.attend(stream)
         return self.out, self.lse, self.idx

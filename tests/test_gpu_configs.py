@@ -62,8 +62,13 @@ def _decode_case(config, **over):
     inp = datagen.make_config(config, **over)
     d = upload_decode(inp)
     step = DecodeStep.from_inputs(d, inp.shapes.k, 1.0 / math.sqrt(inp.shapes.Dqk), inp.shapes.Dv)
-    step.run()
+    step.run()  # fused index + top-k: no score row stored
+    # the two separate calls, for the scores the checks read; their kept sets must be the same
+    step.index()
+    two = torch.empty_like(step.idx)
+    step.topk(out=two)
     torch.cuda.synchronize()
+    assert torch.equal(step.idx, two), "fused index + top-k differs from the two calls"
     return inp, step
 
 
@@ -75,6 +80,10 @@ def test_config1_tiny_fp32_prefill():
     d = upload_prefill(inp)
     pf = Prefill.from_inputs(d, s.k, 1.0 / math.sqrt(s.Dqk), s.Dv)
     pf.run()
+    pf.index()
+    two = torch.empty_like(pf.idx)
+    pf.topk(out=two)
+    assert torch.equal(pf.idx, two), "fused index + top-k differs from the two calls"
     scores = pf.scores.cpu().numpy(); idx = pf.idx.cpu().numpy()
     out = pf.out.cpu().numpy(); lse = pf.lse.cpu().numpy()
     pairs = 0
@@ -125,8 +134,13 @@ def test_config4_prefill_t32768_sampled_rows():
     s = inp.shapes
     d = upload_prefill(inp)
     pf = Prefill.from_inputs(d, s.k, 1.0 / math.sqrt(s.Dqk), s.Dv)
-    pf.run()
+    pf.run()  # blocked fused index + top-k: no T x T buffer
+    pf.index()  # the T x T scores, for the checks below
+    two = torch.empty_like(pf.idx)
+    pf.topk(out=two)
     torch.cuda.synchronize()
+    assert torch.equal(pf.idx, two), "blocked fused index + top-k differs from the two calls"
+    del two
     T = inp.T
     rng = np.random.default_rng(4)
     rows = sorted(set([0, 1, 2046, 2047, 2048, 2049, T - 1] + rng.integers(0, T, 9).tolist()))

@@ -134,8 +134,9 @@ def test_index_scores_generic_fp32():
 @pytest.mark.parametrize("paged", [False, True])
 def test_index_topk_equals_the_two_calls(paged):
     """dsa_index_topk returns exactly dsa_topk(dsa_index_scores(...)) with n_valid = pos + 1:
-    long rows (sampled threshold fed by the indexer's contiguous sample), mid and short rows;
-    two rows are also checked against the oracle's top-k under the band rule."""
+    long rows (the fused call's sample pass, compacting indexer and resolve; no score row is
+    stored), mid and short rows; three rows are also checked against the oracle's top-k under
+    the band rule."""
     import long_context_sparse_06_amd as dsa
     _case(f"index_topk paged={paged}")
     # rows 9..12: 8192 (one workgroup's register select) and 8193..32768 (compaction, since
@@ -149,8 +150,8 @@ def test_index_topk_equals_the_two_calls(paged):
         ps = inp.page_size
         return (inp.block_table[b, s // ps], s % ps)
 
-    # Row 6: its top-k sits in one stretch of 2500 tokens (one or two indexer chunks), so that
-    # chunk's local threshold is high and too few candidates reach it: the full-row fallback.
+    # Row 6: its top-k sits in one stretch of 2500 tokens (one or two indexer chunks), boosted
+    # far above the rest of the row.
     for s_ in range(20000, 22500):
         inp.k_scale[slot(6, s_)] *= np.float32(1000.0)
     inp.q_idx[7] = 0                                   # row 7: every score 0 (all tied)
@@ -175,6 +176,78 @@ def test_index_topk_equals_the_two_calls(paged):
     for b in (0, 3, 6):
         parity.check_index_set(got_np[b], pipeline.decode_scores(inp, b), k, f"row {b}")
     assert np.array_equal(got_np[7], np.arange(k))     # all tied: lowest indices
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_index_topk_sample_cases(paged):
+    """Rows built so the fused call's sample threshold takes each route of its resolve, all
+    compared bit-exactly with the two separate calls (whose own top-k takes the same routes over
+    the stored score rows):
+      row 0  Gaussian: ~2k survivors, resolved in LDS;
+      row 1  the 2048 sample positions (i * n) / 2048 score 1000x higher: fewer than k keys reach
+             the threshold, so the resolve scores the row again and selects from all of it;
+      row 2  the sample positions score 1000x lower: nearly every key lies above the threshold
+             (more than fit in LDS), the same fallback;
+      row 3  every key scores 0 except 100 scattered ones (one in the first chunk): the
+             threshold is 0 itself -- the keys above it plus the first keys equal to it, with
+             chunks walked by ballots where both kinds meet;
+      row 4  every key scores 0 (all tied): the first k positions, copied straight out;
+      row 5  shorter than k: every position."""
+    import dataclasses
+    import long_context_sparse_06_amd as dsa
+    _case(f"index_topk sample cases paged={paged}")
+    n, k = 131072, FULL.k
+    sh = dataclasses.replace(FULL, H=4, Dqk=64, Dv=32)  # attention widths unused here
+    lengths = np.array([n, n, n, n, n, 1000])
+    inp = datagen.make_decode(len(lengths), None, sh, seed=57, lengths=lengths, paged=paged)
+
+    def slots(b, pos):  # storage indices of tokens `pos` of sequence b in k_scale
+        pos = np.asarray(pos)
+        if inp.block_table is None:
+            return (np.full_like(pos, b), pos)
+        ps = inp.page_size
+        return (inp.block_table[b, pos // ps], pos % ps)
+
+    samp = (np.arange(2048, dtype=np.int64) * n) // 2048
+    inp.k_scale[slots(1, samp)] *= np.float32(1000.0)
+    inp.k_scale[slots(2, samp)] *= np.float32(1e-3)
+    rng = np.random.default_rng(58)
+    hot = np.concatenate([[5], rng.choice(np.arange(4096, n), 99, replace=False)])
+    cold = np.setdiff1d(np.arange(n), hot)
+    inp.k_scale[slots(3, cold)] = 0.0
+    inp.k_scale[slots(4, np.arange(n))] = 0.0
+    d = upload_decode(inp)
+    B = d.B
+    cache = dsa.Cache(d.keys, d.k_scale, d.block_table, d.page_size, d.seq_stride)
+    scores = torch.empty((B, d.ld), device="cuda")
+    dsa.dsa_index_scores(dsa.E4M3, d.q_idx, d.q_scale, d.w, cache, d.row_seq, d.row_pos, B, FULL.HI,
+                         FULL.dI, scores, d.ld)
+    ref_idx = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    tw = dsa.dsa_topk_workspace_size(B, d.ld, k)
+    tws = torch.empty(max(tw, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_topk(scores, d.ld, d.n_valid, B, k, ref_idx, tws, tw)
+    fw = dsa.dsa_index_topk_workspace_size(B, d.ld, k)
+    fws = torch.full((fw,), 0xA5, dtype=torch.uint8, device="cuda")  # stale bytes must not matter
+    got = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    for rep in range(2):  # a second call over the first one's leftovers
+        dsa.dsa_index_topk(dsa.E4M3, d.q_idx, d.q_scale, d.w, cache, d.row_seq, d.row_pos, B, FULL.HI,
+                           FULL.dI, k, got, fws, fw)
+        got_np, ref_np = got.cpu().numpy(), ref_idx.cpu().numpy()
+        for b in range(B):
+            assert np.array_equal(got_np[b], ref_np[b]), f"rep {rep} row {b}: differs from the two calls"
+    sc = scores.cpu().numpy()
+    # the rows really take the routes named above (bounds from the sample's own order)
+    ks = -(-2 * k * 2048 // n)
+    s1 = np.sort(sc[1, samp])[::-1]
+    assert (sc[1, :n] >= s1[ks + ks // 4]).sum() < k, "row 1 is not a sample underflow"
+    s2 = np.sort(sc[2, samp])[::-1]
+    assert (sc[2, :n] > s2[ks - 1]).sum() > 12288, "row 2 is not a sample overflow"
+    assert (sc[3, :n] > 0).sum() == 100 and (sc[4, :n] == 0).all()
+    for b in (0, 1, 2, 3):
+        parity.check_index_set(got_np[b], pipeline.decode_scores(inp, b), k, f"row {b}")
+    assert set(hot.tolist()) <= set(got_np[3].tolist())
+    assert np.array_equal(got_np[4], np.arange(k))
+    assert np.array_equal(got_np[5], np.concatenate([np.arange(1000), np.full(k - 1000, -1)]))
 
 
 def test_index_topk_many_rows():
