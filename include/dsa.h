@@ -186,18 +186,20 @@ dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, c
  * steps, indexing then selection, as one stage), with n_valid[r] = row_pos[r] + 1.  The result is exactly
  * that of the two calls (same scores, same selection rule).
  *
- * On the fast indexer shape (e4m3, H_I = 64, d_I = 128) with fewer than 512 rows (decode) no
- * score row is stored: inside the indexer's launch, one workgroup per row scores 1024 evenly
- * spaced sample keys and publishes a threshold expected to keep about 3k keys, while the other
- * workgroups score the row and write only the keys at or above it (with their positions) to
- * `ws`; a second launch selects the top k among them.  Where the sample misleads (fewer than k
- * keys reach the threshold, or more than 12288 with at least k above it) that launch scores
- * the row again and selects from all of it: the result never depends on the sample.  The
- * threshold hand-off uses words in `ws` that each call clears for the next: any contents are
- * correct, but a workspace that starts zeroed avoids the slow path on its first call.  Otherwise
- * (prefill-sized calls, other shapes) the rows are scored into `ws` a block at a time (at
- * most 256 MiB of scores per block) and each block is selected before the next is scored,
- * so the workspace does not grow with R x capacity.
+ * On the fast indexer shape (e4m3, H_I = 64, d_I = 128) with fewer than 512 rows (decode) and
+ * a capacity above 32768 no score row is stored: inside the indexer's launch, one workgroup
+ * per row scores 1024 evenly spaced sample keys and publishes a threshold expected to keep
+ * about 3k keys, while the other workgroups score the row and write only the keys at or above
+ * it (with their positions) to `ws`; a second launch selects the top k among them.  Where the
+ * sample misleads (fewer than k keys reach the threshold, or more than 12288 with at least k
+ * above it) that launch scores the row again and selects from all of it: the result never
+ * depends on the sample.  The threshold hand-off uses words in `ws` that each call clears for
+ * the next: any contents are correct, but a workspace that starts zeroed avoids the slow path
+ * on its first call.  Otherwise (prefill-sized calls; capacities up to 32768, where one
+ * workgroup per row selects from the score row faster than the compaction; other shapes) the
+ * rows are scored into `ws` a block at a time (at most 256 MiB of scores per block) and each
+ * block is selected before the next is scored, so the workspace does not grow with
+ * R x capacity.
  *
  *   arguments as dsa_index_scores (the keys cache's capacity plays the role of ld) and dsa_topk
  *   idx [R, k] int32 output, as dsa_topk

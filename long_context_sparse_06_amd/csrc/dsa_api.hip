@@ -132,16 +132,22 @@ dsa_status dsa_sparse_mla_prefill(dsa_dtype dt, const void* q, const void* kv, c
 }
 
 namespace {
-// The fused call on the fast indexer shape with few rows (decode) stores no score row: a
-// sample pass, the compacting indexer and the resolve (dsa::launch_index_topk_fused).  Other
-// calls (many rows: prefill; other shapes) score a block of rows into the workspace and
-// select from it, block after block, so the score buffer is bounded by kScoreBlockBytes
-// instead of growing with R x n_max.
+// The fused call on the fast indexer shape with few, long rows (decode) stores no score row:
+// the compacting indexer with its sample workgroups, then the resolve
+// (dsa::launch_index_topk_fused).  Other calls (many rows: prefill; capacities up to 32768;
+// other shapes) score a block of rows into the workspace and select from it, block after
+// block, so the score buffer is bounded by kScoreBlockBytes instead of growing with R x n_max.
 constexpr size_t kScoreBlockBytes = size_t(256) << 20;
 constexpr int kRowGroup = 7;  // rows per workgroup of the many-rows indexer: blocks keep its groups whole
 
 bool fused_fast(dsa_dtype dt, int H_I, int d_I) { return dt == DSA_E4M3 && H_I == 64 && d_I == 128; }
-bool fused_decode(int R, int64_t cap) { return R < dsa::index_rows_kernel_min() && dsa::index_topk_fused_ok(R, cap); }
+// Rows up to 32768 keys are selected by one workgroup each straight from their score row (no
+// compaction pass), which measured faster than the sampled compaction at that length: the
+// sample workgroup's latency is longer than the short chunks' scoring.
+constexpr int64_t kFusedMinCapacity = 32768;
+bool fused_decode(int R, int64_t cap) {
+  return R < dsa::index_rows_kernel_min() && cap > kFusedMinCapacity && dsa::index_topk_fused_ok(R, cap);
+}
 
 int block_rows(int R, int64_t cap) {
   int64_t rb = (int64_t)(kScoreBlockBytes / (sizeof(float) * (size_t)cap)) / kRowGroup * kRowGroup;

@@ -30,6 +30,12 @@ constexpr int kCompactTrips = 8;  // most trips per wave of the compacting index
 // partial sums of each group and leaves group g's totals in lanes 16*g .. 16*g+15, so the 64
 // scores of the trip leave in one coalesced 256-byte store.
 //
+// Chunks of the compacting indexer: the row bound's tb 64-key trips split as evenly as the
+// trips allow, chunk c starting at key chunk_start(c, tb, nc).
+__device__ __forceinline__ int64_t chunk_start(int c, int tb, int nc) {
+  return (int64_t)kIdxBatch * (((int64_t)c * tb) / nc);
+}
+
 // COMPACT (the fused index + top-k call): no score is stored.  The grid has R extra blocks
 // in front: block r scores row r's kCompactSample evenly spaced keys (positions
 // (i * n) / kCompactSample) and publishes the row's threshold theta -- about 3k survivors
@@ -119,9 +125,18 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
   const int r = blk / n_chunks;
   const int chunk = blk % n_chunks;
   const int64_t n = (int64_t)row_pos[r] + 1;
-  const int64_t wg_begin = (int64_t)chunk * keys_per_wg;
+  // COMPACT: keys_per_wg is the row bound's trip count tb and chunk c covers trips
+  // [c * tb / n_chunks, (c + 1) * tb / n_chunks) (chunk_start).
+  int64_t wg_begin, wg_full;
+  if (COMPACT) {
+    wg_begin = chunk_start(chunk, keys_per_wg, n_chunks);
+    wg_full = chunk_start(chunk + 1, keys_per_wg, n_chunks);
+  } else {
+    wg_begin = (int64_t)chunk * keys_per_wg;
+    wg_full = wg_begin + keys_per_wg;
+  }
   if (wg_begin >= n || (COMPACT && n <= min_n)) return;
-  const int64_t wg_end = min(wg_begin + keys_per_wg, n);
+  const int64_t wg_end = min(wg_full, n);
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wave = tid / WAVE;
@@ -148,9 +163,16 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
   float wr[4][4];
   load_query(sq, sw, col, grp, qa, wr);
   const float qs = q_scale ? q_scale[r] : 1.0f;
-  const int per_wave = keys_per_wg / kIdxWaves;
-  const int64_t wbeg = wg_begin + (int64_t)wave * per_wave;
-  const int64_t wend = min(wbeg + per_wave, n);
+  int64_t wbeg, wend;
+  if (COMPACT) {  // wave w of a chunk of nt trips: trips [w * nt / 8, (w + 1) * nt / 8)
+    const int nt = (int)((wg_full - wg_begin) / kIdxBatch);
+    wbeg = wg_begin + (int64_t)kIdxBatch * (wave * nt / kIdxWaves);
+    wend = min(wg_begin + (int64_t)kIdxBatch * ((wave + 1) * nt / kIdxWaves), n);
+  } else {
+    const int per_wave = keys_per_wg / kIdxWaves;
+    wbeg = wg_begin + (int64_t)wave * per_wave;
+    wend = min(wbeg + per_wave, n);
+  }
 
   auto row_of = [&](int64_t s) -> int64_t {
     if (PAGED) {
@@ -530,26 +552,40 @@ hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, cons
   return hipGetLastError();
 }
 
+// Resident workgroups of this kernel on the chip: two per CU (its register use) x 256 CUs.
+constexpr int kIndexSlots = 512;
+
+int index_compact_chunks(int R, int64_t n_bound) {
+  const int64_t tb = (n_bound + kIdxBatch - 1) / kIdxBatch;
+  const int64_t nc_min = (tb + kIdxWaves * kCompactTrips - 1) / (kIdxWaves * kCompactTrips);  // <= 8 trips per wave
+  const int64_t nc_max = tb / kIdxWaves > 1 ? tb / kIdxWaves : 1;                              // >= 1 trip per wave
+  // The sample blocks and every chunk of every row in one resident round, when they fit.
+  const int64_t fill = R < kIndexSlots ? (kIndexSlots - R) / R : 1;
+  const int64_t nc = fill < nc_max ? fill : nc_max;
+  return (int)(nc > nc_min ? nc : nc_min);
+}
+
 hipError_t launch_index_fp8_compact(const uint8_t* q, const float* q_scale, const float* w,
                                     const CacheView& keys, const int32_t* row_seq,
                                     const int32_t* row_pos, int R, int64_t n_bound, int64_t ld,
                                     RowHeader* hdr, uint64_t* ready, ChunkCount* counts, uint2* cand,
                                     int min_n, hipStream_t s) {
   const uint8_t* kd = static_cast<const uint8_t*>(keys.data);
-  const int kpw = index_keys_per_wg(R, n_bound);
-  const int n_chunks = (int)((n_bound + kpw - 1) / kpw);
+  const int tb = (int)((n_bound + kIdxBatch - 1) / kIdxBatch);
+  const int n_chunks = index_compact_chunks(R, n_bound);
+  const int max_keys = kIdxBatch * ((tb + n_chunks - 1) / n_chunks);  // longest chunk
   const unsigned grid = (unsigned)R + (unsigned)R * (unsigned)n_chunks;  // sample blocks first
   if (keys.table) {
     const int ps = keys.page_size;
     const int shift = (ps & (ps - 1)) == 0 ? __builtin_ctz(ps) : -1;
-    const size_t lds = sizeof(int) * (size_t)(kpw / ps + 2);
+    const size_t lds = sizeof(int) * (size_t)(max_keys / ps + 2);
     index_fp8_kernel<true, true><<<grid, kIdxWaves * WAVE, lds, s>>>(
         q, q_scale, w, kd, keys.scale, keys.table, keys.max_pages, ps, shift, 0, row_seq, row_pos,
-        nullptr, ld, kpw, n_chunks, hdr, ready, counts, cand, min_n, R);
+        nullptr, ld, tb, n_chunks, hdr, ready, counts, cand, min_n, R);
   } else {
     index_fp8_kernel<false, true><<<grid, kIdxWaves * WAVE, 0, s>>>(
         q, q_scale, w, kd, keys.scale, nullptr, 0, 1, 0, keys.seq_stride, row_seq, row_pos, nullptr,
-        ld, kpw, n_chunks, hdr, ready, counts, cand, min_n, R);
+        ld, tb, n_chunks, hdr, ready, counts, cand, min_n, R);
   }
   return hipGetLastError();
 }

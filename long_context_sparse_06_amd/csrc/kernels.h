@@ -39,10 +39,13 @@ hipError_t launch_index_fp8_h64d128(const uint8_t* q, const float* q_scale, cons
                                     const CacheView& keys, const int32_t* row_seq,
                                     const int32_t* row_pos, int R, int64_t n_bound, float* scores,
                                     int64_t ld, hipStream_t s);
+// Chunks per row of the compacting indexer for R rows of at most n_bound keys; chunk c starts
+// at key 64 * (c * tb / nc), tb = ceil(n_bound / 64).
+int index_compact_chunks(int R, int64_t n_bound);
 // Scores rows longer than min_n without storing them.  R extra workgroups score each row's
 // sample and publish its threshold (hdr[r], and the word ready[r] the scoring workgroups poll);
 // the survivors of that threshold go to the chunk slots of cand [R, ld] with per-chunk counts
-// [R, ceil(n_bound / chunk)].  ready[r] must not hold a published word of an earlier call
+// [R, index_compact_chunks(R, n_bound)].  ready[r] must not hold a published word of an earlier call
 // (the resolve clears it); if it does, chunks may be compacted with a stale threshold, which
 // the resolve detects (ChunkCount::theta) and answers by rescoring the row.
 hipError_t launch_index_fp8_compact(const uint8_t* q, const float* q_scale, const float* w,

@@ -365,6 +365,15 @@ struct Rescore {
   const int32_t* row_seq;  // [R]
 };
 
+// Candidate-slot chunks of a row: the row bound's tb 64-key trips split into nc chunks,
+// chunk j starting at position 64 * (j * tb / nc) (uniform 4096-position chunks: tb = 64 nc).
+struct Chunks {
+  int tb, nc;
+  __device__ int start(int j) const { return 64 * (int)(((int64_t)j * tb) / nc); }
+  // chunks holding positions below n
+  __device__ int count(int n) const { return (int)((((int64_t)n + 63) / 64 * nc + tb - 1) / tb); }
+};
+
 // Scores positions 0 .. n-1 of row r into order-preserving keys keys_out[0 .. n) (all threads
 // of the block; the caller publishes them with a barrier).
 __device__ void rescore_row(const Rescore& rs, int r, int n, uint32_t* __restrict__ keys_out) {
@@ -394,7 +403,7 @@ __device__ void rescore_row(const Rescore& rs, int r, int n, uint32_t* __restric
 // chunk keeps a prefix of its slot -- it has no key equal to theta, or keeps all of them, or
 // has only such keys -- its ids are copied straight out: output position p finds its chunk
 // by binary search over the offsets.  Any other chunk is walked by one wave with ballots.
-__device__ void emit_theta_boundary(const uint2* __restrict__ rcand, int C, int nch, const int* pg,
+__device__ void emit_theta_boundary(const uint2* __restrict__ rcand, const Chunks& C, int nch, const int* pg,
                                     const int* pe, uint32_t theta, int k, int32_t* __restrict__ out) {
   constexpr int NW = kResolveThreads / WAVE;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
@@ -419,7 +428,7 @@ __device__ void emit_theta_boundary(const uint2* __restrict__ rcand, int C, int 
           const int mid = (lo + hi + 1) >> 1;
           if (sb(mid) <= p) lo = mid; else hi = mid - 1;
         }
-        if (direct(lo)) src[u] = lo * C + (p - sb(lo));
+        if (direct(lo)) src[u] = C.start(lo) + (p - sb(lo));
       }
     }
     int v[U];
@@ -434,7 +443,7 @@ __device__ void emit_theta_boundary(const uint2* __restrict__ rcand, int C, int 
     const int et = eqt(j);
     if (direct(j) || g + et == 0) continue;
     const int cnt = g + (pe[j + 1] - pe[j]);
-    const uint2* cj = rcand + (int64_t)j * C;
+    const uint2* cj = rcand + C.start(j);
     int eq_run = 0, sel_run = sb(j);
     for (int i0 = 0; i0 < cnt; i0 += U * WAVE) {
       uint2 v[U];
@@ -460,18 +469,18 @@ __device__ void emit_theta_boundary(const uint2* __restrict__ rcand, int C, int 
 // C is the chunk length of the candidate slots; `row` is the score row, or null in the fused
 // call, whose fallback rescores the row (through rs) into its candidate slots first.
 // kPre x U: chunks per wave and slot rounds per chunk loaded before the counts are known
-// (sized to the launch's chunks: ~4k survivors in 32 chunks of 4096 positions, or ~6k in 64
-// chunks of 2048).
+// (sized to the launch's chunks: ~4k survivors in 32 chunks of 4096 positions, or ~6k in the
+// fused call's 63 chunks of ~2080 at 8 x 131072).
 template <int kPre, int U>
 __device__ void resolve_long_row(const float* __restrict__ row, const Rescore& rs, int64_t ld, int n, int k,
                                  int r, int32_t* __restrict__ out, const RowHeader* __restrict__ hdr,
-                                 const ChunkCount* __restrict__ counts, int max_chunks, int C,
+                                 const ChunkCount* __restrict__ counts, int max_chunks, const Chunks& C,
                                  uint2* __restrict__ cand, uint64_t* __restrict__ ready, uint32_t* smem,
                                  int* hist, uint2* ties, SelState& st) {
   static_assert(kSurvBins <= kPassMax * kHistBins, "the survivor histogram reuses the radix buffers");
   static_assert(kSurvBins == 4 * kResolveThreads, "four survivor bins per thread");
   constexpr int NW = kResolveThreads / WAVE;
-  const int nch = (n + C - 1) / C;
+  const int nch = C.count(n);
   uint32_t* keys = smem;
   int* ids = reinterpret_cast<int*>(smem + kCandCap);
   int* pg = reinterpret_cast<int*>(smem + 2 * kCandCap);  // [nch + 1] survivors above theta before chunk j
@@ -491,9 +500,10 @@ __device__ void resolve_long_row(const float* __restrict__ row, const Rescore& r
 #pragma unroll
   for (int m = 0; m < kPre; ++m) {
     const int j = w + m * NW < nch ? w + m * NW : 0;
-    const int cl = min(C, n - j * C);  // the chunk's length: slots stay in the row
+    const int c0j = C.start(j);
+    const int cl = min(C.start(j + 1), n) - c0j;  // the chunk's length: slots stay in the row
 #pragma unroll
-    for (int u = 0; u < U; ++u) pre[m][u] = rcand[(int64_t)j * C + min(u * WAVE + lane, cl - 1)];
+    for (int u = 0; u < U; ++u) pre[m][u] = rcand[c0j + min(u * WAVE + lane, cl - 1)];
   }
   if (w == 0) {  // exclusive prefixes of the survivor counts, 64 chunks per step
     int cg = 0, ce = 0;
@@ -565,7 +575,7 @@ __device__ void resolve_long_row(const float* __restrict__ row, const Rescore& r
       for (int i0 = j < w + kPre * NW ? U * WAVE : 0; i0 < cj; i0 += U * WAVE) {
         uint2 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = rcand[(int64_t)j * C + min(i0 + u * WAVE + lane, cj - 1)];
+        for (int u = 0; u < U; ++u) v[u] = rcand[C.start(j) + min(i0 + u * WAVE + lane, cj - 1)];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int i = i0 + u * WAVE + lane;
@@ -588,7 +598,7 @@ template <int kPre, int U>
 __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid, int k,
     int32_t* __restrict__ idx, const RowHeader* __restrict__ hdr, const ChunkCount* __restrict__ counts,
-    int max_chunks, int chunk, uint2* __restrict__ cand, uint64_t* __restrict__ ready, int n_off, int long_min,
+    int max_chunks, int tb, uint2* __restrict__ cand, uint64_t* __restrict__ ready, int n_off, int long_min,
     Rescore rs) {
   static_assert(kRowThreads == kResolveThreads, "one kernel serves both paths");
   extern __shared__ uint32_t smem[];  // long rows: survivor keys, ids and chunk offsets
@@ -611,8 +621,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     else select_mid_row<kRowMax / kRowThreads>(row, n, k, out, hist, st);
     return;
   }
-  resolve_long_row<kPre, U>(row, rs, ld, n, k, r, out, hdr, counts, max_chunks, chunk, cand, ready, smem, hist,
-                            ties, st);
+  resolve_long_row<kPre, U>(row, rs, ld, n, k, r, out, hdr, counts, max_chunks, Chunks{tb, max_chunks}, cand,
+                            ready, smem, hist, ties, st);
 }
 
 struct WsLayout {
@@ -622,9 +632,9 @@ struct WsLayout {
 
 // [ready [R] (fused call only)], hdr [R], counts [R, max_chunks], cand [R, ld] (one 8-byte
 // slot per position).
-WsLayout long_ws(int R, int64_t ld, int chunk, bool fused) {
+WsLayout long_ws(int R, int64_t ld, int max_chunks, bool fused) {
   WsLayout L{};
-  L.max_chunks = (int)((ld + chunk - 1) / chunk);
+  L.max_chunks = max_chunks;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   L.ready = 0;
   L.hdr = fused ? up(sizeof(uint64_t) * (size_t)R) : 0;
@@ -636,7 +646,7 @@ WsLayout long_ws(int R, int64_t ld, int chunk, bool fused) {
 
 WsLayout ws_layout(int R, int64_t ld) {
   if (ld <= kRowMax) return WsLayout{};
-  return long_ws(R, ld, kChunk, false);
+  return long_ws(R, ld, (int)((ld + kChunk - 1) / kChunk), false);
 }
 
 size_t finish_lds_bytes(int max_chunks) {
@@ -673,24 +683,25 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid, 
   // Long rows: survivor keys and ids, then the chunk offsets (rows up to kRowMax need none).
   const size_t lds = L.total ? finish_lds_bytes(L.max_chunks) : 0;
   topk_finish_kernel<2, 4><<<R, kRowThreads, lds, s>>>(scores, ld, n_valid, k, idx, hdr, counts, L.max_chunks,
-                                                       kChunk, cand, nullptr, n_off, long_min, Rescore{});
+                                                       kChunk / 64 * L.max_chunks, cand, nullptr, n_off,
+                                                       long_min, Rescore{});
   return hipGetLastError();
 }
 
 // ---- fused index + top-k (fast indexer shape)
 
-size_t index_topk_fused_bytes(int R, int64_t ld) { return long_ws(R, ld, index_keys_per_wg(R, ld), true).total; }
+size_t index_topk_fused_bytes(int R, int64_t ld) { return long_ws(R, ld, index_compact_chunks(R, ld), true).total; }
 
 bool index_topk_fused_ok(int R, int64_t ld) {
-  const int mc = long_ws(R, ld, index_keys_per_wg(R, ld), true).max_chunks;
+  const int mc = index_compact_chunks(R, ld);
   return mc <= kFusedMaxChunks && (int64_t)R * (mc + 1) <= 2147483647LL;
 }
 
 hipError_t launch_index_topk_fused(const uint8_t* q, const float* q_scale, const float* w, const CacheView& keys,
                                    const int32_t* row_seq, const int32_t* row_pos, int R, int64_t ld, int k,
                                    int32_t* idx, void* ws, hipStream_t s) {
-  const int chunk = index_keys_per_wg(R, ld);
-  const WsLayout L = long_ws(R, ld, chunk, true);
+  const WsLayout L = long_ws(R, ld, index_compact_chunks(R, ld), true);
+  const int tb = (int)((ld + 63) / 64);
   char* wsb = static_cast<char*>(ws);
   uint64_t* ready = reinterpret_cast<uint64_t*>(wsb + L.ready);
   RowHeader* hdr = reinterpret_cast<RowHeader*>(wsb + L.hdr);
@@ -704,7 +715,7 @@ hipError_t launch_index_topk_fused(const uint8_t* q, const float* q_scale, const
                                           k, s);
   if (e != hipSuccess) return e;
   topk_finish_kernel<4, 2><<<R, kRowThreads, finish_lds_bytes(L.max_chunks), s>>>(
-      nullptr, ld, row_pos, k, idx, hdr, counts, L.max_chunks, chunk, cand, ready, 1, 0, rs);
+      nullptr, ld, row_pos, k, idx, hdr, counts, L.max_chunks, tb, cand, ready, 1, 0, rs);
   return hipGetLastError();
 }
 
