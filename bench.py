@@ -511,6 +511,20 @@ def prefill(args):
     del sq, sidx, so, sl
     idx_tf = idx_flops / (t_idx * 1e-3) / 1e12
     mla_tf = mla_flops / (t_mla * 1e-3) / 1e12
+    # Counter-derived MFMA busy % of the same kernels from the committed rocprofv3 record (one
+    # counter pass of this command); null when the kernel source changed since it was taken.
+    counters = {"sparse_mla": None, "index": None}
+    try:
+        import hashlib
+        rec = json.load(open(os.path.join(ROOT, "profiles", "mfma_counters_prefill_t32768.json")))
+        for key, r in (("sparse_mla", rec), ("index", rec["indexer"])):
+            src = open(os.path.join(ROOT, r["source"]), "rb").read()
+            if hashlib.sha256(src).hexdigest() == r["source_sha256"]:
+                counters[key] = {"mfma_busy_pct": r["MfmaUtil_pct"], "waves_per_simd": r["waves_per_simd"],
+                                 "lds_bank_conflict_pct": r["LdsBankConflict_pct"], "instance": r["instance"],
+                                 "mfma_flops_counted": r["mfma_flops_counted"]}
+    except (OSError, KeyError, ValueError):
+        pass
     out = {
         "metric": "DSA prefill tokens/s at T=32768 (indexer+top-k+sparse MLA); % MFMA peak",
         "value": T / (total * 1e-3),
@@ -532,9 +546,11 @@ def prefill(args):
         "short_prefill_t2048_attention": short,
         "roofline": {
             "index": {"bound": "mfma", "achieved": idx_tf, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                      "frac": idx_tf / FP8_PEAK_TFLOPS, "alg_flops": idx_flops},
+                      "frac": idx_tf / FP8_PEAK_TFLOPS, "alg_flops": idx_flops,
+                      "counters": counters["index"]},
             "sparse_mla": {"bound": "mfma", "achieved": mla_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": mla_tf / BF16_PEAK_TFLOPS, "alg_flops": mla_flops},
+                           "frac": mla_tf / BF16_PEAK_TFLOPS, "alg_flops": mla_flops,
+                           "counters": counters["sparse_mla"]},
         },
     }
     print(json.dumps(out), flush=True)
