@@ -49,8 +49,9 @@ typedef enum {
   DSA_ERR_DTYPE = 3,       /* dtype not accepted by this entry point                   */
   DSA_ERR_WORKSPACE = 4,   /* workspace pointer NULL or smaller than required          */
   DSA_ERR_LAUNCH = 5,      /* the HIP runtime reported an error after launching        */
-  DSA_ERR_UNSUPPORTED = 6  /* valid but unsupported combination (e.g. an fp32 shape
+  DSA_ERR_UNSUPPORTED = 6, /* valid but unsupported combination (e.g. an fp32 shape
                               beyond the generic kernel's LDS)                         */
+  DSA_ERR_RANGE = 7        /* a validator found an index or page entry out of range    */
 } dsa_status;
 
 typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_E4M3 = 2 } dsa_dtype;
@@ -281,6 +282,30 @@ dsa_status dsa_cache_append(const float* k_new, const void* kv_new, const int32_
 
 /* Static text for a status code ("DSA_OK", ...); never NULL. */
 const char* dsa_status_string(dsa_status status);
+
+/*
+ * dsa_check_indices, dsa_check_block_table -- host-side validators of the device-side values
+ * the kernels trust (see the conventions above: out-of-range indices or page-table entries are
+ * undefined behaviour, they read outside the caches).  They do no GPU work and touch only HOST
+ * memory: the caller copies the arrays to the host first, e.g. in a debug build or before the
+ * first launch on new tables.  Setting DSA_DEBUG_CHECKS=1 makes the Python step classes run
+ * them on every step.  Both return DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE (a size <= 0) or
+ * DSA_ERR_RANGE with *first_bad set to the flat index of the first offending entry (else -1).
+ *
+ * dsa_check_indices: idx [R, k] int32 (host), n_valid [R] int32 (host), as dsa_topk writes and
+ *   the attention calls read them: every entry is -1 or in [0, n_valid[r]).  strict != 0 also
+ *   requires the form dsa_topk produces -- the valid entries ascending without repeats, then
+ *   only -1 (the attention kernels count a repeated index twice).  A negative n_valid[r] is
+ *   reported at index r * k.
+ * dsa_check_block_table: table [B, max_pages] int32 (host), lengths [B] int32 (host, tokens
+ *   cached per sequence): every length lies in [0, max_pages * page_size] (else *first_bad =
+ *   -1 - b) and every page a sequence uses, p < ceil(lengths[b] / page_size), maps into the
+ *   pool: 0 <= table[b * max_pages + p] < pool_pages (else *first_bad = b * max_pages + p).
+ */
+dsa_status dsa_check_indices(const int32_t* idx, int R, int k, const int32_t* n_valid, int strict,
+                             int64_t* first_bad);
+dsa_status dsa_check_block_table(const int32_t* table, int B, int max_pages, const int32_t* lengths,
+                                 int page_size, int64_t pool_pages, int64_t* first_bad);
 
 #ifdef __cplusplus
 }

@@ -21,14 +21,14 @@ __all__ = [
     "dsa_index_topk", "dsa_index_topk_workspace_size", "dsa_indexer_quality",
     "dsa_indexer_quality_workspace_size",
     "dsa_cache_append", "dsa_sparse_mla_decode_noalloc", "dsa_noalloc_scratch_bytes",
-    "dsa_status_string", "exported_symbols",
+    "dsa_status_string", "dsa_check_indices", "dsa_check_block_table", "exported_symbols",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 F32, BF16, E4M3 = 0, 1, 2
 _STATUS = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_DTYPE", "DSA_ERR_WORKSPACE",
-           "DSA_ERR_LAUNCH", "DSA_ERR_UNSUPPORTED"]
+           "DSA_ERR_LAUNCH", "DSA_ERR_UNSUPPORTED", "DSA_ERR_RANGE"]
 
 
 class DSAError(RuntimeError):
@@ -74,6 +74,8 @@ _SIGS = {
     "dsa_sparse_mla_decode_noalloc": (_i32, [_i32, _vp, ctypes.POINTER(_Cache), _vp, _i32, _i32, _i32,
                                              _i32, _i32, _f32, _vp, _vp, _vp]),
     "dsa_status_string": (ctypes.c_char_p, [_i32]),
+    "dsa_check_indices": (_i32, [_vp, _i32, _i32, _vp, _i32, ctypes.POINTER(ctypes.c_int64)]),
+    "dsa_check_block_table": (_i32, [_vp, _i32, _i32, _vp, _i32, _i64, ctypes.POINTER(ctypes.c_int64)]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -247,3 +249,43 @@ def dsa_indexer_quality(q, kv: Cache, scores, ld: int, idx, row_seq, row_pos, R:
         Dqk, k, softmax_scale, _ptr(kl), _ptr(recall), _ptr(kl_rev), _ptr(ws), ws_bytes,
         _stream(stream)))
 
+
+def _host_i32(a):
+    """A C-contiguous int32 numpy copy of a tensor (device tensors are copied to the host)."""
+    import numpy as np
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def dsa_check_indices(idx, n_valid, strict: bool = False) -> None:
+    """Host-side range check of kept-index lists idx [R, k] against n_valid [R] (device tensors
+    are copied to the host first).  Raises DSAError (DSA_ERR_RANGE, with `first_bad` the flat
+    index of the first offending entry) if an entry is out of range -- or, with strict, breaks
+    the ascending, repeat-free, -1-padded form dsa_topk writes."""
+    a, n = _host_i32(idx), _host_i32(n_valid)
+    if a.ndim != 2 or n.shape != (a.shape[0],):
+        raise ValueError("idx must be [R, k] and n_valid [R]")
+    bad = ctypes.c_int64(-1)
+    st = lib().dsa_check_indices(a.ctypes.data, a.shape[0], a.shape[1], n.ctypes.data, int(bool(strict)),
+                                 ctypes.byref(bad))
+    if st != 0:
+        e = DSAError("dsa_check_indices", st)
+        e.first_bad = int(bad.value)
+        raise e
+
+
+def dsa_check_block_table(table, lengths, page_size: int, pool_pages: int) -> None:
+    """Host-side check that every page the sequences use (lengths [B] tokens) maps into a pool
+    of pool_pages pages in table [B, max_pages].  Raises DSAError (DSA_ERR_RANGE, with
+    `first_bad`: the flat table index, or -1 - b for an out-of-range length) otherwise."""
+    t, ln = _host_i32(table), _host_i32(lengths)
+    if t.ndim != 2 or ln.shape != (t.shape[0],):
+        raise ValueError("table must be [B, max_pages] and lengths [B]")
+    bad = ctypes.c_int64(-1)
+    st = lib().dsa_check_block_table(t.ctypes.data, t.shape[0], t.shape[1], ln.ctypes.data, int(page_size),
+                                     int(pool_pages), ctypes.byref(bad))
+    if st != 0:
+        e = DSAError("dsa_check_block_table", st)
+        e.first_bad = int(bad.value)
+        raise e

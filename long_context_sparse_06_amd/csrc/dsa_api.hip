@@ -34,6 +34,7 @@ const char* dsa_status_string(dsa_status s) {
     case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
     case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH";
     case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_RANGE: return "DSA_ERR_RANGE";
   }
   return "DSA_ERR_UNKNOWN";
 }
@@ -272,6 +273,58 @@ dsa_status dsa_cache_append(const float* k_new, const void* kv_new, const int32_
   if (cache_capacity(keys) <= 0 || cache_capacity(kv) <= 0) return DSA_ERR_SHAPE;
   return launched(dsa::launch_cache_append(k_new, static_cast<const uint16_t*>(kv_new), row_seq, row_pos,
                                            R, d_I, Dqk, view(keys), view(kv), stream));
+}
+
+dsa_status dsa_check_indices(const int32_t* idx, int R, int k, const int32_t* n_valid, int strict,
+                             int64_t* first_bad) {
+  if (!idx || !n_valid || !first_bad) return DSA_ERR_NULL;
+  *first_bad = -1;
+  if (R <= 0 || k <= 0) return DSA_ERR_SHAPE;
+  for (int r = 0; r < R; ++r) {
+    const int32_t n = n_valid[r];
+    const int32_t* row = idx + (int64_t)r * k;
+    if (n < 0) {
+      *first_bad = (int64_t)r * k;
+      return DSA_ERR_RANGE;
+    }
+    bool padding = false;  // strict: a -1 was seen, only -1 may follow
+    int32_t prev = -1;
+    for (int j = 0; j < k; ++j) {
+      const int32_t v = row[j];
+      bool bad = v < -1 || v >= n;
+      if (strict && !bad) bad = (v >= 0 && (padding || v <= prev));
+      if (bad) {
+        *first_bad = (int64_t)r * k + j;
+        return DSA_ERR_RANGE;
+      }
+      if (v < 0) padding = true;
+      else prev = v;
+    }
+  }
+  return DSA_OK;
+}
+
+dsa_status dsa_check_block_table(const int32_t* table, int B, int max_pages, const int32_t* lengths,
+                                 int page_size, int64_t pool_pages, int64_t* first_bad) {
+  if (!table || !lengths || !first_bad) return DSA_ERR_NULL;
+  *first_bad = -1;
+  if (B <= 0 || max_pages <= 0 || page_size <= 0 || pool_pages <= 0) return DSA_ERR_SHAPE;
+  for (int b = 0; b < B; ++b) {
+    const int64_t len = lengths[b];
+    if (len < 0 || len > (int64_t)max_pages * page_size) {
+      *first_bad = -1 - (int64_t)b;
+      return DSA_ERR_RANGE;
+    }
+    const int64_t used = (len + page_size - 1) / page_size;
+    for (int64_t p = 0; p < used; ++p) {
+      const int32_t e = table[(int64_t)b * max_pages + p];
+      if (e < 0 || e >= pool_pages) {
+        *first_bad = (int64_t)b * max_pages + p;
+        return DSA_ERR_RANGE;
+      }
+    }
+  }
+  return DSA_OK;
 }
 
 }  // extern "C"

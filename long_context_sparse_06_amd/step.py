@@ -10,15 +10,26 @@ two as the one call dsa_index_topk (same result as the two calls), which at deco
 no score row and at prefill scores a bounded block of rows at a time; index() and topk()
 issue the two calls separately into a full score buffer, for per-stage timing and
 diagnostics -- that buffer ([B, ld] at decode, [T, T] at prefill) is allocated on first use.
+
+With DSA_DEBUG_CHECKS=1 in the environment the classes also run the library's host-side
+validators (which copy to the host and so synchronise): the block table against the caches'
+page pools at construction, and every step's kept indices before the attention reads them.
 """
 from __future__ import annotations
 
+import os
+
 import torch
 
-from . import (BF16, E4M3, F32, Cache, dsa_index_scores, dsa_index_topk,
+from . import (BF16, E4M3, F32, Cache, dsa_check_block_table, dsa_check_indices, dsa_index_scores,
+               dsa_index_topk,
                dsa_index_topk_workspace_size, dsa_sparse_mla_decode,
                dsa_sparse_mla_decode_workspace_size, dsa_sparse_mla_prefill, dsa_topk,
                dsa_topk_workspace_size)
+
+
+def debug_checks() -> bool:
+    return os.environ.get("DSA_DEBUG_CHECKS", "") not in ("", "0")
 
 
 class DecodeStep:
@@ -55,6 +66,10 @@ class DecodeStep:
         mw = dsa_sparse_mla_decode_workspace_size(self.B, self.H, self.Dv, self.k)
         self.mla_ws = torch.empty(max(mw, 1), dtype=torch.uint8, device=dev)
         self.mla_ws_bytes = mw
+        self.debug = debug_checks()
+        if self.debug and block_table is not None:
+            pool = min(keys.numel() // self.dI, kv.numel() // self.Dqk) // int(page_size)
+            dsa_check_block_table(block_table, n_valid, page_size, pool)
 
     @classmethod
     def from_inputs(cls, d, k, softmax_scale, Dv, fp32=False):
@@ -100,6 +115,8 @@ class DecodeStep:
 
     def run(self, stream=None):
         self.index_topk(stream)
+        if self.debug:
+            dsa_check_indices(self.idx, self.n_valid, strict=True)
         self.attend(stream)
         return self.out, self.lse, self.idx
 
@@ -134,6 +151,7 @@ class Prefill:
         odt = torch.float32 if fp32 else torch.bfloat16
         self.out = torch.empty(self.T, self.H, self.Dv, dtype=odt, device=dev)
         self.lse = torch.empty(self.T, self.H, dtype=torch.float32, device=dev)
+        self.debug = debug_checks()
 
     @property
     def scores(self):
@@ -169,5 +187,7 @@ class Prefill:
 
     def run(self, stream=None):
         self.index_topk(stream)
+        if self.debug:
+            dsa_check_indices(self.idx, self.n_valid, strict=True)
         self.attend(stream)
         return self.out, self.lse, self.idx
