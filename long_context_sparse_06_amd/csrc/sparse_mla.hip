@@ -549,9 +549,16 @@ __global__ __launch_bounds__(NW * WAVE) void mla_wide_kernel(
   const int n = lane & 31, h = lane >> 5;  // 32x32 MFMA lane coordinates
   uint32_t* smask = reinterpret_cast<uint32_t*>(MASKED ? srow : srow + tok_per_split);
 
+  // The first batch of this wave's row-list indices goes out before the query loads, whose
+  // issue alone takes thousands of cycles (each touches 32 cache lines): the index round trip
+  // then overlaps it instead of following it.
+  const int32_t* irow = idx + (int64_t)r * k + t_begin;
+  int v_first = -1;
+  if (!MASKED && 64 * w < n_tok) v_first = irow[min(64 * w + lane, n_tok - 1)];
+  __builtin_amdgcn_sched_barrier(0);
   // ---- query fragments (B operand of S^T = K Q^T): lane (n, h) holds, for k-step ks,
-  // q[r, head n of this wave, 16 * ks + 8 * h .. + 7].  Issued first so their latency
-  // overlaps the row list.
+  // q[r, head n of this wave, 16 * ks + 8 * h .. + 7].  Issued before the row list is built
+  // so their latency overlaps it.
   v8bf qf[KS];
   {
     const int hd = hg * HPW + 32 * w + n;
@@ -578,10 +585,9 @@ __global__ __launch_bounds__(NW * WAVE) void mla_wide_kernel(
       }
     }
   } else {
-    const int32_t* irow = idx + (int64_t)r * k + t_begin;
     for (int i0 = 64 * w; i0 < n_tok; i0 += 64 * NW) {
       const int i = i0 + lane;
-      const int v = i < n_tok ? irow[i] : -1;
+      const int v = i < n_tok ? (i0 == 64 * w ? v_first : irow[i]) : -1;
       int row = v;
       if (PAGED && v >= 0) row = table[(int64_t)seq * max_pages + v / page_size] * page_size + v % page_size;
       const uint64_t live = ballot(row >= 0);
@@ -837,47 +843,42 @@ __global__ __launch_bounds__(NW * WAVE) void mla_wide_kernel(
     }
   }
   // The output (or this split's partial) rows go out through LDS: every wave scales its
-  // accumulators and writes them as bf16 into the (now idle) ring, rows padded to 1040 bytes,
-  // then each store instruction writes one head's whole 1 KB row.  Storing straight from the
-  // accumulator layout would spread every instruction's 8-byte pieces over 32 head rows.
-  // Two rounds of HPW / 2 heads (66.5 KB each) fit in the ring.
+  // accumulators and writes them as bf16 into the (now idle) ring, then each store
+  // instruction writes one head's whole 1 KB row.  Storing straight from the accumulator
+  // layout would spread every instruction's 8-byte pieces over 32 head rows.  Two rounds of
+  // NW / 2 head blocks; block bb of a round goes to ring slot bb, its 32 head rows padded to
+  // 1040 bytes (33,280 bytes per slot), so every staging address is a lane base plus a
+  // constant.
   __syncthreads();  // s_fin visible; every wave is done with the ring
-  constexpr int RH = HPW / 2;            // head rows per round
-  constexpr int ROWB = kDv * 2 + 16;     // padded LDS row: 2-way bank conflicts at most
-  static_assert(RH * ROWB <= kNBuf * kBufBytes, "staging fits in the ring");
-  // byte o of the staging area: the ring's slots are separate variables, so o is split into
-  // a slot and an offset (rows never straddle a slot: ROWB-aligned rows are placed per slot)
-  constexpr int RPS = kBufBytes / ROWB;  // rows per slot
-  static_assert((RH + RPS - 1) / RPS <= kNBuf, "rows fit the slots");
-  auto stage_ptr = [&](int o) -> char* {
-    const int row = o / ROWB, off = o - row * ROWB;
-    const int sl = row / RPS, rs = row - sl * RPS;
-    char* base = sl == 0 ? g_ring0 : (sl == 1 ? g_ring1 : g_ring2);
-    return base + rs * ROWB + off;
-  };
+  constexpr int RH = HPW / 2;         // head rows per round
+  constexpr int ROWB = kDv * 2 + 16;  // padded LDS row: 2-way bank conflicts at most
+  static_assert(32 * ROWB <= kBufBytes && NW / 2 <= kNBuf, "a head block's rows fit one slot");
+  auto slot_base = [](int bb) -> char* { return bb == 0 ? g_ring0 : (bb == 1 ? g_ring1 : g_ring2); };
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd) {
 #pragma unroll
     for (int bb = 0; bb < NW / 2; ++bb) {
       const int b = rd * (NW / 2) + bb;
       const float inv = s_fin[b][n];
+      char* srow_b = slot_base(bb) + n * ROWB + 2 * (32 * CB * w + 4 * h);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const v16f& x = acc[cb][b];
-          const uint32_t lo = f32_to_bf16(x[4 * j] * inv) | ((uint32_t)f32_to_bf16(x[4 * j + 1] * inv) << 16);
-          const uint32_t hi = f32_to_bf16(x[4 * j + 2] * inv) | ((uint32_t)f32_to_bf16(x[4 * j + 3] * inv) << 16);
-          const int row = 32 * bb + n, c = 32 * CB * w + 32 * cb + 8 * j + 4 * h;
-          *reinterpret_cast<uint2*>(stage_ptr(row * ROWB + 2 * c)) = make_uint2(lo, hi);
+          const v4bf o4 = {(__bf16)(x[4 * j] * inv), (__bf16)(x[4 * j + 1] * inv), (__bf16)(x[4 * j + 2] * inv),
+                           (__bf16)(x[4 * j + 3] * inv)};
+          *reinterpret_cast<v4bf*>(srow_b + 2 * (32 * cb + 8 * j)) = o4;
         }
     }
     __syncthreads();
-    for (int row = w; row < RH; row += NW) {
-      const int hd = hg * HPW + rd * RH + row;
+#pragma unroll
+    for (int i = 0; i < RH / NW; ++i) {  // row rr: head block rr >> 5 of the round, head rr & 31
+      const int rr = w + NW * i;
+      const int hd = hg * HPW + rd * RH + rr;
       uint16_t* dst = SPLIT ? part_o + (((int64_t)r * n_split + sp) * H + hd) * kDv
                             : out + ((int64_t)r * H + hd) * kDv;
-      const uint4 v = *reinterpret_cast<const uint4*>(stage_ptr(row * ROWB + 16 * lane));
+      const uint4 v = *reinterpret_cast<const uint4*>(slot_base(rr >> 5) + (rr & 31) * ROWB + 16 * lane);
       *reinterpret_cast<uint4*>(dst + 8 * lane) = v;
     }
     if (rd == 0) __syncthreads();  // round 0's rows are read before round 1 overwrites them
