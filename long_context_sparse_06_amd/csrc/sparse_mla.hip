@@ -310,9 +310,22 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   const uint16_t* qrow = q + ((int64_t)r * H + h) * kDqk + (kDqk / 2) * half;
   v8bf qf[kKK];
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(qrow + 8 * grp);
+    // Each quad of lanes (4 hh .. 4 hh + 3) loads one head's 64-byte piece of a k-step, so a
+    // load makes 16 cache-line requests instead of 64 (at start-up every workgroup loads its
+    // queries at once, beside the first gathers); a lane permute then moves piece grp of head
+    // col to lane col + 16 grp, the operand layout.
+    const int hh = lane >> 2, g = lane & 3;
+    const uint4* qp = reinterpret_cast<const uint4*>(qrow + (int64_t)(hh - col) * kDqk) + g;
+    uint4 raw[kKK];
 #pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) qf[kk] = __builtin_bit_cast(v8bf, qp[4 * kk]);
+    for (int kk = 0; kk < kKK; ++kk) raw[kk] = qp[4 * kk];
+    const int src = 4 * col + grp;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+      const uint4 t = make_uint4((uint32_t)__shfl((int)raw[kk].x, src), (uint32_t)__shfl((int)raw[kk].y, src),
+                                 (uint32_t)__shfl((int)raw[kk].z, src), (uint32_t)__shfl((int)raw[kk].w, src));
+      qf[kk] = __builtin_bit_cast(v8bf, t);
+    }
   }
   constexpr int kVSide1 = 14;  // half 1: value tiles below this are on side 1
   v4f acc_o[kDv / 32];         // value tile dt of this half (columns in the epilogue), head col
