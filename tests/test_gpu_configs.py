@@ -117,6 +117,47 @@ def test_config5_ragged_paged_decode():
     _check_decode(inp, step, range(inp.B))
 
 
+def test_decode_step_graph_replays():
+    """The decode step (fused index + top-k, then the split attention) captured in HIP graphs,
+    as bench.py times it, and replayed: every replay must give the eager step's bits (kept
+    set, output, lse).  The fused call clears its own hand-off words, so replays start clean;
+    eager steps and synchronisations run between the replays, and a second step object's
+    graph (its own workspaces, the same kernels) is replayed in between."""
+    from long_context_sparse_06_amd.step import DecodeStep
+    _case("decode step graph replays B=4 L=40000")
+    inp = datagen.make_config(3, B=4, L=40000)
+    d = upload_decode(inp)
+    scale = 1.0 / math.sqrt(inp.shapes.Dqk)
+    st = DecodeStep.from_inputs(d, inp.shapes.k, scale, inp.shapes.Dv)
+    st2 = DecodeStep.from_inputs(d, inp.shapes.k, scale, inp.shapes.Dv)
+    st.run()
+    st2.run()
+    torch.cuda.synchronize()
+    ref = (st.idx.clone(), st.out.clone(), st.lse.clone())
+    g, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run()
+    with torch.cuda.graph(g2):
+        st2.run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.idx.fill_(-7); st.out.fill_(3.0); st.lse.fill_(3.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.idx, ref[0]) and torch.equal(st.out, ref[1]) and torch.equal(st.lse, ref[2]), \
+            f"graph replay {rep}"
+        st2.idx.fill_(-7); st2.out.fill_(3.0)
+        st2.run()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(st2.idx, ref[0]) and torch.equal(st2.out, ref[1])
+        g2.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st2.idx, ref[0]) and torch.equal(st2.out, ref[1]) and torch.equal(st2.lse, ref[2])
+    st.index()  # score rows for the oracle check of the replayed result
+    torch.cuda.synchronize()
+    _check_decode(inp, st, range(inp.B))
+
+
 def test_peaked_decode_stress():
     _case("peaked decode B=4 L=50000")
     inp, step = _decode_case(3, B=4, L=50000, regime="peaked")
