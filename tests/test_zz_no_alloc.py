@@ -1,7 +1,7 @@
 """dsa_sparse_mla_decode_noalloc (split partials in the library's static per-GPU array) gives
 exactly dsa_sparse_mla_decode's output with a caller workspace: on two calls in a row, the
 second with a smaller batch and kept-set size, so the array holds the first call's partials
-when the second runs."""
+when the second runs; and captured in a HIP graph and replayed."""
 import math
 
 import numpy as np
@@ -73,6 +73,46 @@ def test_noalloc_matches_workspace_call_twice():
     assert 0 < dsa.dsa_sparse_mla_decode_workspace_size(2, FULL.H, FULL.Dv, k2) < \
         dsa.dsa_sparse_mla_decode_workspace_size(len(lengths), FULL.H, FULL.Dv, k)
     _both(dsa, d2, tensor(_sets(rng, lengths2, k2)), 2, k2, True)
+
+
+def test_noalloc_under_graph_capture():
+    """The entry point's purpose: a call captured in a HIP graph (nothing allocated inside the
+    capture) and replayed.  Every replay must give the workspace call's bits; eager calls of
+    both entry points and synchronisations run between the replays."""
+    import long_context_sparse_06_amd as dsa
+    rng = np.random.default_rng(85)
+    lengths = np.array([7000, 2100, 40, 5000])
+    B, k = len(lengths), 2048
+    inp = datagen.make_decode(B, None, FULL, seed=86, lengths=lengths, regime="peaked")
+    d = upload_decode(inp)
+    idx = tensor(_sets(rng, lengths, k))
+    scale = 1.0 / math.sqrt(FULL.Dqk)
+    cache = dsa.Cache(d.kv, None, d.block_table, d.page_size, d.seq_stride)
+    wsb = dsa.dsa_sparse_mla_decode_workspace_size(B, FULL.H, FULL.Dv, k)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    ref_o = torch.empty((B, FULL.H, FULL.Dv), dtype=torch.bfloat16, device="cuda")
+    ref_l = torch.empty((B, FULL.H), device="cuda")
+    dsa.dsa_sparse_mla_decode(dsa.BF16, d.q, cache, idx, B, FULL.H, FULL.Dqk, FULL.Dv, k, scale, ref_o, ref_l,
+                              ws, wsb)
+    out = torch.empty_like(ref_o)
+    lse = torch.empty_like(ref_l)
+    # one eager call first (the array's address is looked up on a device's first call)
+    dsa.dsa_sparse_mla_decode_noalloc(dsa.BF16, d.q, cache, idx, B, FULL.H, FULL.Dqk, FULL.Dv, k, scale, out, lse)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dsa.dsa_sparse_mla_decode_noalloc(dsa.BF16, d.q, cache, idx, B, FULL.H, FULL.Dqk, FULL.Dv, k, scale, out,
+                                          lse)
+    for rep in range(3):
+        out.fill_(7.0); lse.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"graph replay {rep}"
+        o2, l2 = torch.empty_like(ref_o), torch.empty_like(ref_l)
+        dsa.dsa_sparse_mla_decode_noalloc(dsa.BF16, d.q, cache, idx, B, FULL.H, FULL.Dqk, FULL.Dv, k, scale, o2, l2)
+        dsa.dsa_sparse_mla_decode(dsa.BF16, d.q, cache, idx, B, FULL.H, FULL.Dqk, FULL.Dv, k, scale, o2, l2, ws, wsb)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, ref_o) and torch.equal(l2, ref_l)
 
 
 def test_noalloc_rejects_sets_beyond_the_array():
