@@ -253,14 +253,8 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
     s_cnt[1][wave] = eq;
   }
   __syncthreads();
-  int off = 0, G = 0, E = 0;
-#pragma unroll
-  for (int v = 0; v < kIdxWaves; ++v) {
-    const int a = s_cnt[0][v], b = s_cnt[1][v];
-    off += v < wave ? a + b : 0;
-    G += a;
-    E += b;
-  }
+  int off, G, E;
+  wave_offsets<kIdxWaves>(s_cnt[0], s_cnt[1], wave, off, G, E);
   uint2* cr = cand + (int64_t)r * ld + wg_begin;
   for (int t = 0; t < nt; ++t) {
     const uint32_t key = s_key[(wave * kCompactTrips + t) * kIdxBatch + lane];

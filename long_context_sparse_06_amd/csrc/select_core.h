@@ -106,9 +106,55 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t v, F op) {
   return op((uint32_t)b[0], (uint32_t)b[1]);
 }
 struct UMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+struct UAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
 struct UMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
 
 __device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// Block-level reductions over the NW per-wave values in LDS, done with lane v standing for wave
+// v (one LDS load, a DPP scan or reduce, a ballot).  Every wave of the block computes them; a
+// scalar walk over the NW values costs each wave ~10 scalar instructions per value, and the CU
+// issues one scalar instruction per SIMD every fourth cycle, so with four waves per SIMD those
+// walks, not the data, set the time of the selection's short phases.
+//
+// Crossing wave of a search from the per-wave totals t[0..NW): the first wave v whose running
+// total reaches `need` (vc = -1 when none does), and the total of the waves before it (of all
+// of them when none does).
+template <int NW>
+__device__ __forceinline__ void crossing_wave(const int* t, int need, int& vc, int& before) {
+  static_assert(NW <= WAVE, "one lane per wave");
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int tv = lane < NW ? t[lane] : 0;
+  const int incl = wave_incl_scan(tv);
+  const uint64_t hit = ballot((lane < NW) & (incl >= need));
+  vc = hit ? (int)__builtin_ctzll(hit) : -1;
+  before = hit ? readlane(incl - tv, vc) : readlane(incl, NW - 1);
+}
+// Minimum (and maximum) of the per-wave values v[0..NW), in every lane.
+template <int NW>
+__device__ __forceinline__ uint32_t block_min(const uint32_t* v) {
+  static_assert(NW <= WAVE, "one lane per wave");
+  const int lane = threadIdx.x & (WAVE - 1);
+  return wave_reduce(lane < NW ? v[lane] : 0xFFFFFFFFu, UMin{});
+}
+template <int NW>
+__device__ __forceinline__ uint32_t block_max(const uint32_t* v) {
+  static_assert(NW <= WAVE, "one lane per wave");
+  const int lane = threadIdx.x & (WAVE - 1);
+  return wave_reduce(lane < NW ? v[lane] : 0u, UMax{});
+}
+// Per-wave counts a[0..NW) and b[0..NW): their totals, and the sum of a + b over the waves
+// before wave w (a compaction's output offset), in every lane.
+template <int NW>
+__device__ __forceinline__ void wave_offsets(const int* a, const int* b, int w, int& off, int& ta, int& tb) {
+  static_assert(NW <= WAVE, "one lane per wave");
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int av = lane < NW ? a[lane] : 0, bv = lane < NW ? b[lane] : 0;
+  const int ia = wave_incl_scan(av), ib = wave_incl_scan(bv);
+  off = readlane(ia - av + ib - bv, w);
+  ta = readlane(ia, NW - 1);
+  tb = readlane(ib, NW - 1);
+}
 
 // The top-k threshold: the selection is { key > T } plus the `need` lowest-index elements
 // equal to T, or exactly { key >= T } when `exact`.  `top` is the largest key seen.
@@ -211,14 +257,8 @@ __device__ Threshold radix_threshold(uint32_t lo, uint32_t hi, int k, int* hist,
     const int incl = wave_incl_scan(local);
     if (lane == WAVE - 1) st.wscan[w] = incl;
     __syncthreads();
-    int before = 0, vc = -1;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const int tv = st.wscan[v];
-      const bool hit = vc < 0 && before + tv >= need;
-      before += (vc < 0 && !hit) ? tv : 0;
-      vc = hit ? v : vc;
-    }
+    int before, vc;
+    crossing_wave<NW>(st.wscan, need, vc, before);
     // Rescan the crossing wave's bins (the same PER per lane that wave read).
     const int first2 = nb - 1 - PER * (vc * WAVE + lane);
     int cb2[PER];
@@ -269,12 +309,7 @@ __device__ Threshold find_threshold(const Src& src, int m, int k, int* hist, Sel
     publish_range<NT>(lmn, lmx, hist, st);
     __syncthreads();
   }
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    lo = min(lo, st.wmin[i]);
-    hi = max(hi, st.wmax[i]);
-  }
+  const uint32_t lo = block_min<NW>(st.wmin), hi = block_max<NW>(st.wmax);
   return radix_threshold<NT>(lo, hi, k, hist, st, slack, [&](uint32_t a, uint32_t b, int s, int* h) {
     for_each_key<NT, 8>(src, m, [&](int, uint32_t key) {
       if (key >= a && key <= b) atomicAdd(&h[(key - a) >> s], 1);
@@ -299,7 +334,8 @@ __device__ void emit_selected(const Src& src, int m, const Threshold& th, SelSta
   const int beg = w * per;
   const int end = min(m, beg + per);
   constexpr int U = 8;  // rounds of 64 whose keys are read before they are used
-  int cgt = 0, ceq = 0;
+  // Per-lane counts, summed over the wave once (a ballot count per round is scalar work)
+  int lgt = 0, leq = 0;
   for (int i0 = beg; i0 < end; i0 += U * WAVE) {
     uint32_t kv[U];
 #pragma unroll
@@ -307,10 +343,11 @@ __device__ void emit_selected(const Src& src, int m, const Threshold& th, SelSta
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool in = i0 + u * WAVE + lane < end;
-      cgt += __popcll(ballot(in & ((kv[u] > T) | (ex & (kv[u] == T)))));
-      ceq += __popcll(ballot(in & !ex & (kv[u] == T)));
+      lgt += (in & ((kv[u] > T) | (ex & (kv[u] == T)))) ? 1 : 0;
+      leq += (in & !ex & (kv[u] == T)) ? 1 : 0;
     }
   }
+  const int cgt = (int)wave_reduce((uint32_t)lgt, UAdd{}), ceq = (int)wave_reduce((uint32_t)leq, UAdd{});
   if (lane == 0) {
     st.wtot[0][w] = cgt;
     st.wtot[1][w] = ceq;
@@ -379,9 +416,7 @@ __device__ RowHeader sample_header(const uint32_t* samp, int ns, int over, uint3
     mn = wave_reduce(mn, UMin{});
     if (lane == 0) st.wred[w] = mn;  // not wmin: slower waves may still read that
     __syncthreads();
-    theta = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) theta = min(theta, st.wred[i]);
+    theta = block_min<NW>(st.wred);
   }
   // Survivor bins span [theta, largest sample] in at most kSurvBins steps of 2^shift;
   // scores above the largest sample land in the last bin.

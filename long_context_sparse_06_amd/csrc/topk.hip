@@ -122,14 +122,8 @@ __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
     st.wtot[1][w] = eq;
   }
   __syncthreads();
-  int off = 0, G = 0, E = 0;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    const int a = st.wtot[0][v], b = st.wtot[1][v];
-    off += v < w ? a + b : 0;
-    G += a;
-    E += b;
-  }
+  int off, G, E;
+  wave_offsets<NW>(st.wtot[0], st.wtot[1], w, off, G, E);
   uint2* cr = cand + (int64_t)r * ld + base;
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
@@ -158,14 +152,8 @@ __device__ __forceinline__ void select_survivors(const uint32_t* keys, const int
   const int incl = wave_incl_scan(hv.x + hv.y + hv.z + hv.w);
   if (lane == WAVE - 1) st.wscan[w] = incl;
   __syncthreads();
-  int before = 0, vc = -1;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    const int tv = st.wscan[v];
-    const bool hit = vc < 0 && before + tv >= k;
-    before += (vc < 0 && !hit) ? tv : 0;
-    vc = hit ? v : vc;
-  }
+  int before, vc;
+  crossing_wave<NW>(st.wscan, k, vc, before);
   const int4 hc = reinterpret_cast<const int4*>(hist)[kResolveThreads - 1 - (vc * WAVE + lane)];
   const int cb[4] = {hc.w, hc.z, hc.y, hc.x};
   int bstar, above, bcnt;
@@ -188,7 +176,7 @@ __device__ __forceinline__ void select_survivors(const uint32_t* keys, const int
     const int per = ((total + NW - 1) / NW + WAVE - 1) / WAVE * WAVE;
     const int beg = w * per;
     const int end = min(total, beg + per);
-    int above_w = 0;
+    int above_l = 0;  // this lane's count, summed over the wave after the pass
     for (int i0 = beg; i0 < end; i0 += 4 * WAVE) {
       uint32_t kv[4];
 #pragma unroll
@@ -197,7 +185,7 @@ __device__ __forceinline__ void select_survivors(const uint32_t* keys, const int
       for (int u = 0; u < 4; ++u) {
         const int i = i0 + u * WAVE + lane;
         const bool ok = i < end;
-        above_w += __popcll(ballot(ok & (kv[u] > t_hi)));
+        above_l += (ok & (kv[u] > t_hi)) ? 1 : 0;
         const bool in = ok & (kv[u] >= t_lo) & (kv[u] <= t_hi);
         const uint64_t im = ballot(in);
         if (im) {  // one slot reservation per wave and round
@@ -208,6 +196,7 @@ __device__ __forceinline__ void select_survivors(const uint32_t* keys, const int
         }
       }
     }
+    const int above_w = (int)wave_reduce((uint32_t)above_l, UAdd{});
     if (lane == 0) st.wtot[0][w] = above_w;
     __syncthreads();
     if (tid < bcnt) {
@@ -300,12 +289,7 @@ __device__ __forceinline__ void select_mid_row(const float* __restrict__ row, in
   }
   publish_range<NT>(lmn, lmx, hist, st);
   __syncthreads();
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    lo = min(lo, st.wmin[i]);
-    hi = max(hi, st.wmax[i]);
-  }
+  const uint32_t lo = block_min<NW>(st.wmin), hi = block_max<NW>(st.wmax);
   const Threshold th = radix_threshold<NT>(lo, hi, k, hist, st, 0, [&](uint32_t a, uint32_t b, int s, int* h) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
@@ -369,7 +353,10 @@ struct Rescore {
 // chunk j starting at position 64 * (j * tb / nc) (uniform 4096-position chunks: tb = 64 nc).
 struct Chunks {
   int tb, nc;
-  __device__ int start(int j) const { return 64 * (int)(((int64_t)j * tb) / nc); }
+  __device__ int start(int j) const {
+    const uint64_t p = (uint64_t)(uint32_t)j * (uint32_t)tb;  // 32-bit division when it fits
+    return 64 * (int)(p >> 32 ? p / (uint32_t)nc : (uint32_t)p / (uint32_t)nc);
+  }
   // chunks holding positions below n
   __device__ int count(int n) const { return (int)((((int64_t)n + 63) / 64 * nc + tb - 1) / tb); }
 };
@@ -497,11 +484,15 @@ __device__ void resolve_long_row(const float* __restrict__ row, const Rescore& r
   const ChunkCount c0 = (w == 0 && lane < nch) ? rc[lane] : ChunkCount{0u, 0u, rh.theta, 0u};
   if (ready && tid == 0) ready[r] = 0;  // the next call's scoring blocks wait for a fresh threshold
   uint2 pre[kPre][U];
+  // Starts of those chunks and of the chunks after them, lane 2m (+1) for the m-th: divisions
+  // in parallel on the vector unit rather than one scalar division per chunk in every wave.
+  static_assert(2 * kPre <= WAVE, "one lane per chunk start");
+  const int jm = w + (lane >> 1) * NW;
+  const int cs = C.start((lane < 2 * kPre && jm < nch ? jm : 0) + (lane & 1));
 #pragma unroll
   for (int m = 0; m < kPre; ++m) {
-    const int j = w + m * NW < nch ? w + m * NW : 0;
-    const int c0j = C.start(j);
-    const int cl = min(C.start(j + 1), n) - c0j;  // the chunk's length: slots stay in the row
+    const int c0j = readlane(cs, 2 * m);
+    const int cl = min(readlane(cs, 2 * m + 1), n) - c0j;  // the chunk's length: slots stay in the row
 #pragma unroll
     for (int u = 0; u < U; ++u) pre[m][u] = rcand[c0j + min(u * WAVE + lane, cl - 1)];
   }
