@@ -363,6 +363,26 @@ __device__ void emit_selected(const Src& src, int m, const Threshold& th, SelSta
   const int eq_before = readlane(eq_before_v, w);
   const int sel_before = readlane(sel_before_v, w);
   int eq_run = 0, sel_run = 0;
+  if (ex) {  // the selection is { key >= T }: no tie bookkeeping
+    for (int i0 = beg; i0 < end; i0 += U * WAVE) {
+      uint32_t kv[U];
+      int iv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = min(i0 + u * WAVE + lane, end - 1);
+        kv[u] = src.key(e);
+        iv[u] = src.id(e);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool sel = (i0 + u * WAVE + lane < end) & (kv[u] >= T);
+        const uint64_t selm = ballot(sel);
+        if (sel) out[sel_before + sel_run + mask_rank(selm)] = iv[u];
+        sel_run += __popcll(selm);
+      }
+    }
+    return;
+  }
   for (int i0 = beg; i0 < end; i0 += U * WAVE) {
     uint32_t kv[U];
     int iv[U];

@@ -300,12 +300,13 @@ __device__ __forceinline__ void select_mid_row(const float* __restrict__ row, in
   const uint32_t T = th.T;
   const bool ex = th.exact;
   const int need = ex ? 0 : th.need;
-  int cgt = 0, ceq = 0;
+  int lgt = 0, leq = 0;  // per-lane counts, summed over the wave once
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    cgt += __popcll(ballot((key[j] > T) | (ex & (key[j] == T))));
-    ceq += __popcll(ballot(!ex & (key[j] == T)));
+    lgt += ((key[j] > T) | (ex & (key[j] == T))) ? 1 : 0;
+    leq += (!ex & (key[j] == T)) ? 1 : 0;
   }
+  const int cgt = (int)wave_reduce((uint32_t)lgt, UAdd{}), ceq = (int)wave_reduce((uint32_t)leq, UAdd{});
   if (lane == 0) {
     st.wtot[0][w] = cgt;
     st.wtot[1][w] = ceq;
@@ -323,11 +324,21 @@ __device__ __forceinline__ void select_mid_row(const float* __restrict__ row, in
   const int sel_before_v = wave_incl_scan(sel_v) - sel_v;
   const int eq_before = readlane(eq_before_v, w);
   int sel_run = readlane(sel_before_v, w);
+  if (ex) {  // the selection is { key >= T }: no tie bookkeeping (the usual case)
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool sel = key[j] >= T2;
+      const uint64_t selm = ballot(sel);
+      if (sel) out[sel_run + mask_rank(selm)] = beg + j * WAVE + lane;
+      sel_run += __popcll(selm);
+    }
+    return;
+  }
   int eq_run = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const bool gt = (key[j] > T2) | (ex & (key[j] == T2));
-    const bool eq = !ex & (key[j] == T2);
+    const bool gt = key[j] > T2;
+    const bool eq = key[j] == T2;
     const uint64_t eqm = ballot(eq);
     const bool sel = gt | (eq & (eq_before + eq_run + mask_rank(eqm) < need));
     const uint64_t selm = ballot(sel);
