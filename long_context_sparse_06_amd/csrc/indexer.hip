@@ -242,12 +242,13 @@ __global__ __launch_bounds__(kIdxWaves * WAVE) void index_fp8_kernel(
   __syncthreads();
   const uint32_t theta = s_theta;
   __shared__ int s_cnt[2][kIdxWaves];
-  int gt = 0, eq = 0;
+  int lgt = 0, leq = 0;  // per-lane counts, summed over the wave once
   for (int t = 0; t < nt; ++t) {
     const uint32_t key = s_key[(wave * kCompactTrips + t) * kIdxBatch + lane];
-    gt += __popcll(ballot(key > theta));
-    eq += __popcll(ballot(key == theta));
+    lgt += key > theta ? 1 : 0;
+    leq += key == theta ? 1 : 0;
   }
+  const int gt = (int)wave_reduce((uint32_t)lgt, UAdd{}), eq = (int)wave_reduce((uint32_t)leq, UAdd{});
   if (lane == 0) {
     s_cnt[0][wave] = gt;
     s_cnt[1][wave] = eq;

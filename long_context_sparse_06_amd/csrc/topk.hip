@@ -110,13 +110,14 @@ __global__ __launch_bounds__(kLongThreads) void topk_prep_kernel(
   const RowHeader rh = sample_header<kLongThreads>(samp, kSample, 2, lmn, lmx, n, k, hist, st);
   const uint32_t theta = rh.theta;
   if (c == 0 && tid == 0) hdr[r] = rh;
-  int gt = 0, eq = 0;
+  int lgt = 0, leq = 0;  // per-lane counts, summed over the wave once
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
     const bool in = wb + it * WAVE + lane < end;
-    gt += __popcll(ballot(in & (key[it] > theta)));
-    eq += __popcll(ballot(in & (key[it] == theta)));
+    lgt += (in & (key[it] > theta)) ? 1 : 0;
+    leq += (in & (key[it] == theta)) ? 1 : 0;
   }
+  const int gt = (int)wave_reduce((uint32_t)lgt, UAdd{}), eq = (int)wave_reduce((uint32_t)leq, UAdd{});
   if (lane == 0) {
     st.wtot[0][w] = gt;
     st.wtot[1][w] = eq;
