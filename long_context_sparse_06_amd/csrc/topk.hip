@@ -557,35 +557,41 @@ __device__ void resolve_long_row(const float* __restrict__ row, const Rescore& r
     // Wave w copies chunks w, w + NW, ...: the preloaded slots first, then (for chunks
     // with more survivors, or beyond the first kPre) U loads per lane per round trip.
     auto off = [&](int j) { return pg[j] + pe[j]; };
+    // Offsets and survivor counts of this wave's first kPre chunks, lane m for the m-th (one
+    // LDS read per lane instead of scalar reads of every chunk in every wave).
+    const int jl = w + lane * NW;
+    const bool lv = lane < kPre && jl < nch;
+    const int o_l = lv ? off(jl) : 0;
+    const int c_l = lv ? off(jl + 1) - o_l : 0;
 #pragma unroll
     for (int m = 0; m < kPre; ++m) {
-      const int j = w + m * NW;
-      if (j < nch) {
-        const int o = off(j), cj = min(off(j + 1) - o, U * WAVE);
+      const int o = readlane(o_l, m), cj = min(readlane(c_l, m), U * WAVE);  // 0: no such chunk
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int i = u * WAVE + lane;
-          if (i < cj) {
-            keys[o + i] = pre[m][u].x;
-            ids[o + i] = (int)pre[m][u].y;
-            atomicAdd(&hist[min((pre[m][u].x - rh.theta) >> rh.shift, (uint32_t)(kSurvBins - 1))], 1);
-          }
+      for (int u = 0; u < U; ++u) {
+        const int i = u * WAVE + lane;
+        if (i < cj) {
+          keys[o + i] = pre[m][u].x;
+          ids[o + i] = (int)pre[m][u].y;
+          atomicAdd(&hist[min((pre[m][u].x - rh.theta) >> rh.shift, (uint32_t)(kSurvBins - 1))], 1);
         }
       }
     }
-    for (int j = w; j < nch; j += NW) {
-      const int o = off(j), cj = off(j + 1) - o;
-      for (int i0 = j < w + kPre * NW ? U * WAVE : 0; i0 < cj; i0 += U * WAVE) {
-        uint2 v[U];
+    // The rest: survivors past the preloaded slots, and chunks past the first kPre.
+    if (ballot(c_l > U * WAVE) || w + kPre * NW < nch) {
+      for (int j = w; j < nch; j += NW) {
+        const int o = off(j), cj = off(j + 1) - o;
+        for (int i0 = j < w + kPre * NW ? U * WAVE : 0; i0 < cj; i0 += U * WAVE) {
+          uint2 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = rcand[C.start(j) + min(i0 + u * WAVE + lane, cj - 1)];
+          for (int u = 0; u < U; ++u) v[u] = rcand[C.start(j) + min(i0 + u * WAVE + lane, cj - 1)];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int i = i0 + u * WAVE + lane;
-          if (i < cj) {
-            keys[o + i] = v[u].x;
-            ids[o + i] = (int)v[u].y;
-            atomicAdd(&hist[min((v[u].x - rh.theta) >> rh.shift, (uint32_t)(kSurvBins - 1))], 1);
+          for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * WAVE + lane;
+            if (i < cj) {
+              keys[o + i] = v[u].x;
+              ids[o + i] = (int)v[u].y;
+              atomicAdd(&hist[min((v[u].x - rh.theta) >> rh.shift, (uint32_t)(kSurvBins - 1))], 1);
+            }
           }
         }
       }
