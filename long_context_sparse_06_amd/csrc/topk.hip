@@ -723,7 +723,7 @@ hipError_t launch_index_topk_fused(const uint8_t* q, const float* q_scale, const
   hipError_t e = launch_index_fp8_compact(q, q_scale, w, keys, row_seq, row_pos, R, ld, ld, hdr, ready, counts, cand,
                                           k, s);
   if (e != hipSuccess) return e;
-  topk_finish_kernel<4, 2><<<R, kRowThreads, finish_lds_bytes(L.max_chunks), s>>>(
+  topk_finish_kernel<4, 3><<<R, kRowThreads, finish_lds_bytes(L.max_chunks), s>>>(
       nullptr, ld, row_pos, k, idx, hdr, counts, L.max_chunks, tb, cand, ready, 1, 0, rs);
   return hipGetLastError();
 }
