@@ -473,28 +473,39 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
   // Split partials hold this split's own normalized output (bf16, like the final output)
   // and its (max, sum) in fp32; the merge weights each by sum * 2^(max - overall max).
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  if (SPLIT) {
-    const int64_t pr = ((int64_t)r * n_split + sp) * H + h;
-    uint16_t* po = part_o + pr * kDv;
+  // The 64 head rows go out through the idle ring: each wave writes its bf16 pieces into the
+  // head's row (rows 0..31 in slot 0, 32..63 in slot 1, padded to 1040 bytes), then every
+  // store instruction writes one whole 1 KB row.  Storing from the accumulator layout would
+  // spread each instruction's 8-byte pieces over 16 head rows.
+  constexpr int ROWB = kDv * 2 + 16;
+  static_assert(32 * ROWB <= kBufBytes, "32 head rows fit one slot");
+  __syncthreads();  // every compute wave is done with the ring (the copy wave has left)
+  {
+    char* srow_h = (hb >> 1 ? g_ring1 : g_ring0) + (16 * (hb & 1) + col) * ROWB;
 #pragma unroll
     for (int dt = 0; dt < kDv / 32; ++dt) {
       const uint32_t lo = f32_to_bf16(acc_o[dt][0] * inv) | ((uint32_t)f32_to_bf16(acc_o[dt][1] * inv) << 16);
       const uint32_t hi = f32_to_bf16(acc_o[dt][2] * inv) | ((uint32_t)f32_to_bf16(acc_o[dt][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(po + vcol(dt)) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(srow_h + 2 * vcol(dt)) = make_uint2(lo, hi);
     }
-    if (grp == 0 && half == 0) {
+  }
+  if (grp == 0 && half == 0) {
+    if (SPLIT) {
+      const int64_t pr = ((int64_t)r * n_split + sp) * H + h;
       part_ml[2 * pr] = m_run;
       part_ml[2 * pr + 1] = l;
+    } else if (lse) {
+      lse[(int64_t)r * H + h] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
     }
-  } else {
-    uint16_t* op = out + ((int64_t)r * H + h) * kDv;
+  }
+  __syncthreads();
 #pragma unroll
-    for (int dt = 0; dt < kDv / 32; ++dt) {
-      const uint32_t lo = f32_to_bf16(acc_o[dt][0] * inv) | ((uint32_t)f32_to_bf16(acc_o[dt][1] * inv) << 16);
-      const uint32_t hi = f32_to_bf16(acc_o[dt][2] * inv) | ((uint32_t)f32_to_bf16(acc_o[dt][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(op + vcol(dt)) = make_uint2(lo, hi);
-    }
-    if (lse && grp == 0 && half == 0) lse[(int64_t)r * H + h] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+  for (int i = 0; i < kHeadsPerWg / kMlaWaves; ++i) {  // row rr of the workgroup's 64 heads
+    const int rr = w + kMlaWaves * i;
+    const int hd = hg * kHeadsPerWg + rr;
+    uint16_t* dst = SPLIT ? part_o + (((int64_t)r * n_split + sp) * H + hd) * kDv : out + ((int64_t)r * H + hd) * kDv;
+    const uint4 v = *reinterpret_cast<const uint4*>((rr >> 5 ? g_ring1 : g_ring0) + (rr & 31) * ROWB + 16 * lane);
+    *reinterpret_cast<uint4*>(dst + 8 * lane) = v;
   }
 }
 
