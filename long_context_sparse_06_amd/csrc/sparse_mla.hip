@@ -237,52 +237,52 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(
       if (ntiles > 0) issue_row((lane & 31) < n_tok ? (lane & 31) : -1, g_ring0);
       if (ntiles > 1) issue_row(32 + (lane & 31) < n_tok ? 32 + (lane & 31) : -1, g_ring1);
     } else {
-    // The first batch of the row list (tokens 0 .. U * 64 - 1) is loaded before any copy goes
-    // out: loads and copies retire in issue order, so list loads issued after the 72 copies of
-    // tiles 0 and 1 could only be waited for once both tiles had landed, which held tile 0's
-    // hand-over back until tile 1 was in LDS too.
-    constexpr int U = 8;
-    int id[U];
+      // The first batch of the row list (tokens 0 .. U * 64 - 1) is loaded before any copy goes
+      // out: loads and copies retire in issue order, so list loads issued after the 72 copies of
+      // tiles 0 and 1 could only be waited for once both tiles had landed, which held tile 0's
+      // hand-over back until tile 1 was in LDS too.
+      constexpr int U = 8;
+      int id[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) id[u] = u * WAVE < n_tok ? irow[min(u * WAVE + lane, n_tok - 1)] : -1;
-    __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of the copies
-    // Tiles 0 and 1 straight from the first 64 indices (token = lane).
-    {
-      const int v = lane < n_tok ? id[0] : -1;
-      const int row = resolve(v);
-      const uint64_t live = ballot(row >= 0);
-      if (live) last = 63 - (int)__builtin_clzll(live);
-      if (lane < n_tok) srow[lane] = row;
-      if (lane == 0) {
-        if (ntiles > 0) smask[0] = (uint32_t)live;
-        if (ntiles > 1) smask[1] = (uint32_t)(live >> 32);
-      }
-      // lane l needs token l & 31 (tile 0) and 32 + (l & 31) (tile 1)
-      const v2i sw = __builtin_amdgcn_permlane32_swap(row, row, false, false);
-      if (ntiles > 0) issue_row(sw[0], g_ring0);
-      if (ntiles > 1) issue_row(sw[1], g_ring1);
-    }
-    // Row list entries of tokens i0 + 64 u + lane (u >= u0) from id[].
-    auto list = [&](int i0, auto u0) {
-#pragma unroll
-      for (int u = decltype(u0)::value; u < U; ++u) {
-        const int i = i0 + u * WAVE + lane;
-        const int row = resolve(i < n_tok ? id[u] : -1);
+      for (int u = 0; u < U; ++u) id[u] = u * WAVE < n_tok ? irow[min(u * WAVE + lane, n_tok - 1)] : -1;
+      __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of the copies
+      // Tiles 0 and 1 straight from the first 64 indices (token = lane).
+      {
+        const int v = lane < n_tok ? id[0] : -1;
+        const int row = resolve(v);
         const uint64_t live = ballot(row >= 0);
-        if (live) last = i0 + u * WAVE + 63 - (int)__builtin_clzll(live);
-        if (i < n_tok) srow[i] = row;
-        const int t0 = (i0 + u * WAVE) / kTok;
-        if (lane == 0 && t0 < ntiles) smask[t0] = (uint32_t)live;
-        if (lane == 0 && t0 + 1 < ntiles) smask[t0 + 1] = (uint32_t)(live >> 32);
+        if (live) last = 63 - (int)__builtin_clzll(live);
+        if (lane < n_tok) srow[lane] = row;
+        if (lane == 0) {
+          if (ntiles > 0) smask[0] = (uint32_t)live;
+          if (ntiles > 1) smask[1] = (uint32_t)(live >> 32);
+        }
+        // lane l needs token l & 31 (tile 0) and 32 + (l & 31) (tile 1)
+        const v2i sw = __builtin_amdgcn_permlane32_swap(row, row, false, false);
+        if (ntiles > 0) issue_row(sw[0], g_ring0);
+        if (ntiles > 1) issue_row(sw[1], g_ring1);
       }
-    };
-    list(0, std::integral_constant<int, 1>{});
-    // Later batches (splits of more than U * 64 tokens), 8 tokens per lane per batch.
-    for (int i0 = U * WAVE; i0 < n_tok; i0 += U * WAVE) {
+      // Row list entries of tokens i0 + 64 u + lane (u >= u0) from id[].
+      auto list = [&](int i0, auto u0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) id[u] = irow[min(i0 + u * WAVE + lane, n_tok - 1)];  // unconditional: no wait between batch members
-      list(i0, std::integral_constant<int, 0>{});
-    }
+        for (int u = decltype(u0)::value; u < U; ++u) {
+          const int i = i0 + u * WAVE + lane;
+          const int row = resolve(i < n_tok ? id[u] : -1);
+          const uint64_t live = ballot(row >= 0);
+          if (live) last = i0 + u * WAVE + 63 - (int)__builtin_clzll(live);
+          if (i < n_tok) srow[i] = row;
+          const int t0 = (i0 + u * WAVE) / kTok;
+          if (lane == 0 && t0 < ntiles) smask[t0] = (uint32_t)live;
+          if (lane == 0 && t0 + 1 < ntiles) smask[t0 + 1] = (uint32_t)(live >> 32);
+        }
+      };
+      list(0, std::integral_constant<int, 1>{});
+      // Later batches (splits of more than U * 64 tokens), 8 tokens per lane per batch.
+      for (int i0 = U * WAVE; i0 < n_tok; i0 += U * WAVE) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) id[u] = irow[min(i0 + u * WAVE + lane, n_tok - 1)];  // unconditional: no wait between batch members
+        list(i0, std::integral_constant<int, 0>{});
+      }
     }
     // Tiles run: through the last kept token, at least one (tiles 0 and 1 are already in
     // flight; the last hand-over drains whatever was issued).
