@@ -508,24 +508,36 @@ __device__ void resolve_long_row(const float* __restrict__ row, const Rescore& r
 #pragma unroll
     for (int u = 0; u < U; ++u) pre[m][u] = rcand[c0j + min(u * WAVE + lane, cl - 1)];
   }
+  // Survivors past the preloaded slots are gathered by all waves together as one flat range:
+  // rf[j] counts those of the chunks before j.  It lives in the survivor histogram's unused
+  // tail (the radix select clears the whole buffer before it uses it), so rows of more
+  // chunks than that tail holds keep the gather of one wave per chunk.
+  int* rf = hist + kSurvBins;
+  const bool flat = nch < kPassMax * kHistBins - kSurvBins;
   if (w == 0) {  // exclusive prefixes of the survivor counts, 64 chunks per step
-    int cg = 0, ce = 0;
+    int cg = 0, ce = 0, cr = 0;
     bool stale = false;  // a chunk compacted with another threshold than the row's
     for (int j0 = 0; j0 < nch; j0 += WAVE) {
       const int j = j0 + lane;
       const ChunkCount cj = j0 == 0 ? c0 : (j < nch ? rc[j] : ChunkCount{0u, 0u, rh.theta, 0u});
       stale = stale || cj.theta != rh.theta;
       const int ig = wave_incl_scan((int)cj.gt), ie = wave_incl_scan((int)cj.eq);
+      const int cnt = (int)(cj.gt + cj.eq);
+      const int rj = cnt - (j < kPre * NW ? min(cnt, U * WAVE) : 0);
+      const int ir = wave_incl_scan(rj);
       if (j < nch) {
         pg[j] = cg + ig - (int)cj.gt;
         pe[j] = ce + ie - (int)cj.eq;
+        if (flat) rf[j] = cr + ir - rj;
       }
       cg += __shfl(ig, WAVE - 1);
       ce += __shfl(ie, WAVE - 1);
+      cr += __shfl(ir, WAVE - 1);
     }
     if (lane == 0) {
       pg[nch] = ballot(stale) ? -1 : cg;  // -1: the survivors are not one threshold's
       pe[nch] = ce;
+      if (flat) rf[nch] = cr;
     }
   }
   reinterpret_cast<int4*>(hist)[tid] = make_int4(0, 0, 0, 0);
@@ -576,8 +588,40 @@ __device__ void resolve_long_row(const float* __restrict__ row, const Rescore& r
         }
       }
     }
-    // The rest: survivors past the preloaded slots, and chunks past the first kPre.
-    if (ballot(c_l > U * WAVE) || w + kPre * NW < nch) {
+    // The rest: survivors past the preloaded slots, and chunks past the first kPre.  Thread t
+    // takes flat positions t, t + 1024, ... of the rest and finds its chunk by binary search
+    // over rf, so a row whose survivors crowd into a few chunks (a short row keeps nearly
+    // every key) still gathers them with every wave instead of one wave per chunk.
+    if (flat) {
+      const int rest = rf[nch];
+      for (int i0 = 0; i0 < rest; i0 += U * kResolveThreads) {
+        uint2 v[U];
+        int dst[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          // Positions past the rest load the last one (so every load issues) and are dropped.
+          const int i = i0 + u * kResolveThreads + tid;
+          const int ic = min(i, rest - 1);
+          int lo = 0, hi = nch - 1;  // the last chunk whose rest starts at or before ic
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (rf[mid] <= ic) lo = mid; else hi = mid - 1;
+          }
+          const int o = off(lo);
+          const int e = (lo < kPre * NW ? min(off(lo + 1) - o, U * WAVE) : 0) + (ic - rf[lo]);
+          v[u] = rcand[C.start(lo) + e];
+          dst[u] = i < rest ? o + e : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (dst[u] >= 0) {
+            keys[dst[u]] = v[u].x;
+            ids[dst[u]] = (int)v[u].y;
+            atomicAdd(&hist[min((v[u].x - rh.theta) >> rh.shift, (uint32_t)(kSurvBins - 1))], 1);
+          }
+        }
+      }
+    } else if (ballot(c_l > U * WAVE) || w + kPre * NW < nch) {
       for (int j = w; j < nch; j += NW) {
         const int o = off(j), cj = off(j + 1) - o;
         for (int i0 = j < w + kPre * NW ? U * WAVE : 0; i0 < cj; i0 += U * WAVE) {
