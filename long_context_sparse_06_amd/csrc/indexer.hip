@@ -65,6 +65,18 @@ __device__ void compact_sample_block(int r, const uint8_t* __restrict__ q, const
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int col = lane & 15, grp = lane >> 4;
   const int seq = row_seq[r];
+  // Cache rows of this lane's sampled keys (four per trip) and of the key whose scale it
+  // applies (one per trip), for both trips, found before the query is staged: with a
+  // paged cache each is a block-table read, and issuing them all at once keeps them to one
+  // round trip instead of a table read ahead of every trip's key loads.
+  int64_t krow[2][4], srow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j0 = (2 * wave + t) * kIdxBatch;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) krow[t][u] = kr.row(seq, (int64_t)(j0 + 16 * u + col) * n / kCompactSample);
+    srow[t] = kr.row(seq, (int64_t)(j0 + lane) * n / kCompactSample);
+  }
   for (int i = tid; i < 64 * 128 / 16; i += kIdxWaves * WAVE)
     reinterpret_cast<uint4*>(sq)[i] = reinterpret_cast<const uint4*>(q + (int64_t)r * (64 * 128))[i];
   if (tid < 64) sw[tid] = w[(int64_t)r * 64 + tid];
@@ -81,8 +93,8 @@ __device__ void compact_sample_block(int r, const uint8_t* __restrict__ q, const
   for (int t = 0; t < 2; ++t) {
     const int j0 = (2 * wave + t) * kIdxBatch;
     v8i kb[4];
-    load_trip(kdata, kr, seq, col, grp, [&](int j) { return (int64_t)(j0 + j) * n / kCompactSample; }, kb);
-    const float ks = kscale ? kscale[kr.row(seq, (int64_t)(j0 + lane) * n / kCompactSample)] : 1.0f;
+    load_rows(kdata, krow[t], grp, kb);
+    const float ks = kscale ? kscale[srow[t]] : 1.0f;
     const uint32_t key = float_key(scaled_score(trip_scores(qa, wr, kb), ks, qs));
     samp[j0 + lane] = key;
     lmn = min(lmn, key);

@@ -84,6 +84,17 @@ struct KeyRows {
   }
 };
 
+// Loads lane (col, grp)'s key operand of one trip from cache rows rows[u] (key 16*u + col).
+__device__ __forceinline__ void load_rows(const uint8_t* __restrict__ kdata, const int64_t (&rows)[4], int grp,
+                                          v8i (&kb)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint4* p = reinterpret_cast<const uint4*>(kdata + rows[u] * 128 + 32 * grp);
+    const uint4 a = p[0], b = p[1];
+    kb[u] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  }
+}
+
 // Loads lane (col, grp)'s key operand of one trip whose keys are at logical positions pos(j),
 // j = 16*u + col (u < 4); positions are the caller's, already clamped into the row.
 template <class Pos>
