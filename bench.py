@@ -264,6 +264,27 @@ def main():
     cb.record(stream)
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * (1 << 30) / (ca.elapsed_time(cb) * 1e6)
+
+    # ---- achievable streaming-read rate on the step's own caches: dsa_read_probe (every load
+    # one contiguous 1 KB, the indexer's residency) over each copy's key cache in turn, as a
+    # graph of back-to-back launches, HIP events around its replays on this stream
+    sink = torch.empty(dsa.dsa_read_probe_sink_words(), dtype=torch.int32, device=dev)
+    key_bufs = [c.keys for c in copies]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for kb_ in key_bufs:
+            dsa.dsa_read_probe(kb_, sink)
+    gr.replay()
+    torch.cuda.synchronize()
+    ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ra.record(stream)
+    for _ in range(10):
+        gr.replay()
+    rb.record(stream)
+    torch.cuda.synchronize()
+    read_us = ra.elapsed_time(rb) * 1e3 / (10 * len(key_bufs))
+    read_gbs = key_bufs[0].numel() * key_bufs[0].element_size() / (read_us * 1e3)
+    del gr, sink
     del src_b, dst_b
 
     # ---- the fused index + top-k call beside the two separate calls: each as a graph of one
@@ -406,7 +427,9 @@ def main():
                           "frac": roof_us / (ms_per_step * 1e3),
                           "achievable_copy_GBs": copy_gbs,
                           "frac_of_achievable": step_bytes / (copy_gbs * 1e3) / (ms_per_step * 1e3),
-                          "index_frac_of_achievable": achieved / copy_gbs},
+                          "index_frac_of_achievable": achieved / copy_gbs,
+                          "achievable_read_GBs": read_gbs, "read_probe_us": read_us,
+                          "index_frac_of_achievable_read": achieved / read_gbs},
         "step_us_spread": spread,
         "index_topk_fused_vs_separate": fused_cmp,
         "indexer_quality": quality,

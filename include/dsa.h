@@ -280,6 +280,23 @@ dsa_status dsa_cache_append(const float* k_new, const void* kv_new, const int32_
                             const int32_t* row_pos, int R, int d_I, int Dqk, const dsa_cache* keys,
                             const dsa_cache* kv, hipStream_t stream);
 
+/*
+ * dsa_read_probe -- a measurement, not a step of the path: reads `bytes` bytes at `buf` once
+ * and writes to sink[w], for each of its dsa_read_probe_sink_words() workgroups w, the XOR of
+ * the 32-bit words that workgroup read.  The XOR of all sink words is the XOR of every 32-bit
+ * word of the buffer, so a host check shows that all of it was read.  Timing launches of it
+ * gives the rate at which this GPU streams a buffer of that size: every load instruction reads
+ * one contiguous 1 KB (non-temporal), eight in flight per wave, two 512-thread workgroups per
+ * CU.  It is the practical ceiling that the bandwidth-bound indexer scan is compared with.
+ *
+ *   buf   device, 16-byte aligned, `bytes` a positive multiple of 1024; only read
+ *   sink  device uint32 [dsa_read_probe_sink_words()], fully overwritten
+ *
+ * Errors: DSA_ERR_NULL (buf or sink NULL), DSA_ERR_SHAPE (size or alignment), DSA_ERR_LAUNCH.
+ */
+int dsa_read_probe_sink_words(void);
+dsa_status dsa_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Static text for a status code ("DSA_OK", ...); never NULL. */
 const char* dsa_status_string(dsa_status status);
 

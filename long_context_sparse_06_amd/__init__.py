@@ -21,6 +21,7 @@ __all__ = [
     "dsa_index_topk", "dsa_index_topk_workspace_size", "dsa_indexer_quality",
     "dsa_indexer_quality_workspace_size",
     "dsa_cache_append", "dsa_sparse_mla_decode_noalloc", "dsa_noalloc_scratch_bytes",
+    "dsa_read_probe", "dsa_read_probe_sink_words",
     "dsa_status_string", "dsa_check_indices", "dsa_check_block_table", "exported_symbols",
 ]
 
@@ -73,6 +74,8 @@ _SIGS = {
     "dsa_noalloc_scratch_bytes": (_sz, []),
     "dsa_sparse_mla_decode_noalloc": (_i32, [_i32, _vp, ctypes.POINTER(_Cache), _vp, _i32, _i32, _i32,
                                              _i32, _i32, _f32, _vp, _vp, _vp]),
+    "dsa_read_probe_sink_words": (_i32, []),
+    "dsa_read_probe": (_i32, [_vp, _i64, _vp, _vp]),
     "dsa_status_string": (ctypes.c_char_p, [_i32]),
     "dsa_check_indices": (_i32, [_vp, _i32, _i32, _vp, _i32, ctypes.POINTER(ctypes.c_int64)]),
     "dsa_check_block_table": (_i32, [_vp, _i32, _i32, _vp, _i32, _i64, ctypes.POINTER(ctypes.c_int64)]),
@@ -140,6 +143,17 @@ class Cache:
 
 
 # --------------------------------------------------------------------------- the ABI
+def dsa_read_probe_sink_words() -> int:
+    return int(lib().dsa_read_probe_sink_words())
+
+
+def dsa_read_probe(buf, sink, stream=None):
+    """Measurement only: streams `buf` (a device tensor, its size a multiple of 1024 bytes) once
+    and writes per-workgroup XOR words to `sink` (uint32 [dsa_read_probe_sink_words()])."""
+    _check("dsa_read_probe", lib().dsa_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                  _stream(stream)))
+
+
 def dsa_status_string(status: int) -> str:
     return lib().dsa_status_string(status).decode()
 

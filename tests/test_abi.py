@@ -119,6 +119,14 @@ def test_host_validation_paths():
     assert L.dsa_cache_append(FAKE, FAKE, FAKE, FAKE, 4, 8192, 576, ctypes.byref(ks), ctypes.byref(kv), None) == 2
     assert L.dsa_cache_append(FAKE, FAKE, FAKE, FAKE, 4, 128, 576, ctypes.byref(ks), ctypes.byref(bad), None) == 2
 
+    # read probe (measurement only)
+    assert L.dsa_read_probe_sink_words() > 0
+    assert L.dsa_read_probe(None, 1024, FAKE, None) == 1
+    assert L.dsa_read_probe(FAKE, 1024, None, None) == 1
+    assert L.dsa_read_probe(FAKE, 1000, FAKE, None) == 2
+    assert L.dsa_read_probe(FAKE, 0, FAKE, None) == 2
+    assert L.dsa_read_probe(FAKE + 4, 1024, FAKE, None) == 2
+
 
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(dsa, "LIB_PATH", "/nonexistent/libdsa.so")
