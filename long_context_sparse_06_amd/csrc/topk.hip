@@ -566,8 +566,8 @@ __device__ void resolve_long_row(const float* __restrict__ row, const Rescore& r
     return;
   }
   {
-    // Wave w copies chunks w, w + NW, ...: the preloaded slots first, then (for chunks
-    // with more survivors, or beyond the first kPre) U loads per lane per round trip.
+    // Wave w copies the preloaded slots of chunks w, w + NW, ... (its first kPre); the rest --
+    // survivors past those slots, and chunks beyond the first kPre per wave -- follows below.
     auto off = [&](int j) { return pg[j] + pe[j]; };
     // Offsets and survivor counts of this wave's first kPre chunks, lane m for the m-th (one
     // LDS read per lane instead of scalar reads of every chunk in every wave).
